@@ -1,0 +1,265 @@
+"""Independent checks of the CPU oracle (shared by the pin tests and the mutant test).
+
+Each check compares the oracle with something other than itself:
+  * dense softmax attention written with numpy (the method with nothing
+    skipped is plain attention; with a mask it is attention with the skipped
+    tiles' logits at -inf -- the masked-softmax formulation of the skill page);
+  * the hand-derived worked examples in tests/golden;
+  * a closed form of the running max (max over the later live tiles);
+  * consequences the pages fix (monotone masks, the e^tau bound on a marked
+    tile's probabilities, the drop bound, invariance under tile size).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from oracle import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def bits_of(mask_words, tk):
+    m = np.asarray(mask_words).view(np.uint32)
+    out = np.zeros((m.shape[0], tk), bool)
+    for kt in range(tk):
+        out[:, kt] = (m[:, kt // 32] >> np.uint32(kt % 32)) & np.uint32(1)
+    return out
+
+
+def words_of(bits):
+    rows, tk = bits.shape
+    W = -(-tk // 32)
+    w = np.zeros((rows, W), np.uint64)
+    for kt in range(tk):
+        w[:, kt // 32] |= bits[:, kt].astype(np.uint64) << np.uint64(kt % 32)
+    return w.astype(np.uint32)
+
+
+def to64(x):
+    if isinstance(x, torch.Tensor):
+        return x.detach().to(torch.float64).cpu().numpy()
+    return np.asarray(x, np.float64)
+
+
+def dense_reference(q, k, v, scale, skip_bits=None, BM=None, BN=None):
+    """Brute-force attention with numpy: logits of skipped tiles set to -inf.
+
+    Returns out [B,N,H,D], lse [B,H,N] and the probabilities [B,H,N,N]."""
+    q, k, v = to64(q), to64(k), to64(v)
+    B, N, H, D = q.shape
+    s = scale * np.einsum("bnhe,bmhe->bhnm", q, k)
+    if skip_bits is not None:
+        Tq, Tk = -(-N // BM), -(-N // BN)
+        sb = skip_bits.reshape(B, H, Tq, Tk)
+        full = np.repeat(np.repeat(sb, BM, axis=2), BN, axis=3)[:, :, :N, :N]
+        s = np.where(full, -np.inf, s)
+    m = s.max(axis=-1, keepdims=True)
+    mf = np.where(np.isfinite(m), m, 0.0)
+    p = np.exp(s - mf)
+    l = p.sum(axis=-1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        prob = np.where(l > 0, p / np.where(l > 0, l, 1.0), 0.0)
+        lse = np.where(l[..., 0] > 0, mf[..., 0] + np.log(np.where(l[..., 0] > 0, l[..., 0], 1.0)), -np.inf)
+    out = np.einsum("bhnm,bmhe->bnhe", prob, v)
+    return out, lse, prob
+
+
+def closed_form_margins(q, k, scale, BM, BN, skip_bits):
+    """margin(qt, kt) = max_r [ max_{c in kt} s[r,c] - max_{c in live tiles after kt} s[r,c] ].
+
+    The running max seen by a tile in a last-to-first sweep is the max over the
+    live tiles with a larger index; written here as that max, not as a loop
+    that updates a running value.  NaN for skipped tiles."""
+    q, k = to64(q), to64(k)
+    B, N, H, D = q.shape
+    Tq, Tk = -(-N // BM), -(-N // BN)
+    s = scale * np.einsum("bnhe,bmhe->bhnm", q, k)
+    pad = np.full((B, H, Tq * BM, Tk * BN), -np.inf)
+    pad[:, :, :N, :N] = s
+    tiles = pad.reshape(B, H, Tq, BM, Tk, BN)
+    loc = tiles.max(axis=5)                        # [B,H,Tq,BM,Tk] local row max
+    sb = skip_bits.reshape(B, H, Tq, Tk)
+    live_loc = np.where(sb[:, :, :, None, :], -np.inf, loc)
+    out = np.full((B, H, Tq, Tk), np.nan)
+    for kt in range(Tk):
+        later = live_loc[..., kt + 1:].max(axis=-1) if kt + 1 < Tk else np.full(loc.shape[:-1], -np.inf)
+        with np.errstate(invalid="ignore"):
+            d = loc[..., kt] - later                    # [B,H,Tq,BM]
+        valid_rows = (np.arange(Tq)[:, None] * BM + np.arange(BM)[None, :]) < N   # [Tq,BM]
+        d = np.where(valid_rows[None, None], d, -np.inf)
+        mg = d.max(axis=-1)
+        out[..., kt] = np.where(sb[..., kt], np.nan, mg)
+    return out.reshape(B * H * Tq, Tk)
+
+
+def load_golden():
+    with open(os.path.join(GOLDEN, "qkskip_worked_examples.json")) as f:
+        return json.load(f)
+
+
+def _tau(x):
+    return -math.inf if x == "-inf" else float(x)
+
+
+def run_golden(lib=None):
+    """Run every worked example; return a list of failure strings."""
+    doc = load_golden()
+    fails = []
+    rng = np.random.default_rng(0)
+    for case in doc["cases"]:
+        N, BM, BN = case["N"], case["BM"], case["BN"]
+        qm = np.asarray(case["q"], np.float64)[None, :, None, :]        # [1,N,1,N]
+        km = np.eye(N)[None, :, None, :]
+        vm = rng.standard_normal((1, N, 1, N))
+        Tq, Tk = -(-N // BM), -(-N // BN)
+        variants = [("checks", case["mask_in"])]
+        if "checks_without_mask_in" in case:
+            variants.append(("checks_without_mask_in", []))
+        for key, skipped in variants:
+            bits = np.zeros((Tq, Tk), bool)
+            for qt, kt in skipped:
+                bits[qt, kt] = True
+            for chk in case[key]:
+                tau = _tau(chk["tau"])
+                r = oracle.fwd(qm, km, vm, BM, BN, tau, 1.0, mask_in=words_of(bits), lib=lib)
+                newly = bits_of(r["mask_out"], Tk) & ~bits
+                want = np.zeros((Tq, Tk), bool)
+                for qt, kt in chk["newly"]:
+                    want[qt, kt] = True
+                if not np.array_equal(newly, want):
+                    fails.append("%s/%s tau=%s: newly %s want %s" % (case["name"], key, chk["tau"],
+                                                                    np.argwhere(newly).tolist(), chk["newly"]))
+                for tile, val in chk.get("margins", {}).items():
+                    qt, kt = (int(x) for x in tile.split(","))
+                    got = r["margin"][qt, kt]
+                    exp_v = math.inf if val == "inf" else float(val)
+                    if not (got == exp_v):
+                        fails.append("%s/%s margin %s = %r want %r" % (case["name"], key, tile, got, exp_v))
+                # the output of every worked example is plain masked attention
+                o_ref, _, _ = dense_reference(qm, km, vm, 1.0, bits.reshape(-1, Tk), BM, BN)
+                o, _ = oracle.unpack_rows(r, 1, N, 1, BM)
+                if not np.allclose(o, o_ref, atol=1e-12, rtol=0):
+                    fails.append("%s/%s: output differs from masked dense attention" % (case["name"], key))
+    return fails
+
+
+def random_case(seed, B, N, H, D, scale_in=1.0, dtype=torch.float64):
+    g = torch.Generator().manual_seed(seed)
+    q = (scale_in * torch.randn(B, N, H, D, generator=g, dtype=torch.float64)).to(dtype)
+    k = (scale_in * torch.randn(B, N, H, D, generator=g, dtype=torch.float64)).to(dtype)
+    v = torch.randn(B, N, H, D, generator=g, dtype=torch.float64).to(dtype)
+    return q, k, v
+
+
+def check_dense(lib=None, cases=None):
+    """tau = -inf and an empty mask: the oracle is plain softmax attention."""
+    fails = []
+    cases = cases or [(0, 2, 37, 3, 8, 8, 4), (1, 1, 64, 2, 16, 16, 16), (2, 1, 5, 1, 4, 4, 2),
+                      (3, 2, 100, 2, 8, 32, 16), (4, 1, 1, 1, 4, 4, 4), (5, 1, 70, 1, 32, 16, 64)]
+    for seed, B, N, H, D, BM, BN in cases:
+        q, k, v = random_case(seed, B, N, H, D, scale_in=1.5)
+        scale = 1.0 / math.sqrt(D)
+        r = oracle.fwd(q, k, v, BM, BN, -math.inf, scale, lib=lib)
+        o, lse = oracle.unpack_rows(r, B, N, H, BM)
+        o_ref, lse_ref, _ = dense_reference(q, k, v, scale)
+        if not np.allclose(o, o_ref, atol=1e-12, rtol=1e-12):
+            fails.append("dense out case %d: max err %.3g" % (seed, np.abs(o - o_ref).max()))
+        if not np.allclose(lse, lse_ref, atol=1e-12, rtol=1e-12):
+            fails.append("dense lse case %d" % seed)
+        if np.any(bits_of(r["mask_out"], -(-N // BN))):
+            fails.append("dense case %d marked a tile at tau=-inf" % seed)
+    return fails
+
+
+def check_masked_and_rule(lib=None, seeds=range(6)):
+    """Random masks and thresholds: masked dense attention, closed-form margins,
+    monotone masks, the e^tau bound and the first-visited-tile rule."""
+    fails = []
+    for seed in seeds:
+        rng = np.random.default_rng(100 + seed)
+        B, H = 1 + seed % 2, 1 + seed % 3
+        N = int(rng.integers(9, 90))
+        D = int(rng.choice([4, 8, 16]))
+        BM, BN = int(rng.choice([4, 8, 16])), int(rng.choice([4, 8, 16]))
+        q, k, v = random_case(seed, B, N, H, D, scale_in=2.0)
+        scale = 1.0 / math.sqrt(D)
+        Tq, Tk = -(-N // BM), -(-N // BN)
+        bits = rng.random((B * H * Tq, Tk)) < 0.3
+        tau = float(rng.choice([-4.0, -2.0, -1.0, -0.25]))
+        r = oracle.fwd(q, k, v, BM, BN, tau, scale, mask_in=words_of(bits), lib=lib)
+        o, lse = oracle.unpack_rows(r, B, N, H, BM)
+        o_ref, lse_ref, prob = dense_reference(q, k, v, scale, bits, BM, BN)
+        if not np.allclose(o, o_ref, atol=1e-12, rtol=1e-12):
+            fails.append("masked out seed %d err %.3g" % (seed, np.nanmax(np.abs(o - o_ref))))
+        if not np.array_equal(np.isneginf(lse), np.isneginf(lse_ref)) or not np.allclose(
+                np.where(np.isfinite(lse), lse, 0), np.where(np.isfinite(lse_ref), lse_ref, 0), atol=1e-12):
+            fails.append("masked lse seed %d" % seed)
+        cf = closed_form_margins(q, k, scale, BM, BN, bits)
+        got = r["margin"]
+        same_nan = np.array_equal(np.isnan(got), np.isnan(cf))
+        fin = np.isfinite(cf) & np.isfinite(got)
+        if not same_nan or not np.array_equal(np.isposinf(got), np.isposinf(cf)) or \
+                not np.allclose(got[fin], cf[fin], atol=1e-9, rtol=0):
+            fails.append("margins differ from closed form, seed %d" % seed)
+        out_bits = bits_of(r["mask_out"], Tk)
+        if np.any(bits & ~out_bits):
+            fails.append("mask_out dropped an input mark, seed %d" % seed)
+        newly = out_bits & ~bits
+        want = (~bits) & (np.nan_to_num(cf, nan=np.inf) < tau)
+        clear = np.abs(np.nan_to_num(cf, nan=np.inf, posinf=1e300) - tau) > 1e-9
+        if np.any((newly != want) & clear):
+            fails.append("decisions differ from the closed form, seed %d" % seed)
+        # a newly marked tile: each of its probabilities this step is below e^tau
+        pb = prob.reshape(B * H, N, N)
+        for row, kt in np.argwhere(newly):
+            bh, qt = divmod(int(row), Tq)
+            rr = slice(qt * BM, min(N, (qt + 1) * BM))
+            cc = slice(kt * BN, min(N, (kt + 1) * BN))
+            if not np.all(pb[bh, rr, cc] < math.exp(tau)):
+                fails.append("marked tile above e^tau, seed %d" % seed)
+                break
+        # the first visited live tile of a row is never marked; a row with a live
+        # tile keeps at least one
+        for row in range(B * H * Tq):
+            live = [kt for kt in range(Tk - 1, -1, -1) if not bits[row, kt]]
+            if live and newly[row, live[0]]:
+                fails.append("first visited tile marked, seed %d row %d" % (seed, row))
+            if live and out_bits[row].all():
+                fails.append("row emptied by the rule, seed %d row %d" % (seed, row))
+    return fails
+
+
+def check_tile_invariance(lib=None):
+    """With nothing skipped the output does not depend on the tile grid."""
+    q, k, v = random_case(7, 1, 77, 2, 8, scale_in=1.5)
+    outs = []
+    for BM, BN in ((4, 4), (8, 16), (32, 8), (128, 128)):
+        r = oracle.fwd(q, k, v, BM, BN, -math.inf, 0.5, lib=lib)
+        outs.append(oracle.unpack_rows(r, 1, 77, 2, BM)[0])
+    return [] if all(np.allclose(outs[0], o, atol=1e-13) for o in outs[1:]) else ["tile-size dependence"]
+
+
+def check_edge_cases(lib=None):
+    """Padding bits past the last tile are cleared; a fully skipped row gives 0 / -inf;
+    an input mark is never removed."""
+    fails = []
+    q, k, v = random_case(2, 1, 40, 1, 4)            # Tk = 5 with 8-wide tiles
+    words = np.full((5, 1), 0xFFFFFFE0, np.uint32)   # only padding bits set
+    r = oracle.fwd(q, k, v, 8, 8, -math.inf, 0.5, mask_in=words, lib=lib)
+    if np.any(r["mask_out"] != 0):
+        fails.append("padding bits survive")
+    q, k, v = random_case(1, 1, 16, 1, 4)
+    bits = np.ones((2, 2), bool)
+    r = oracle.fwd(q, k, v, 8, 8, -3.0, 0.5, mask_in=words_of(bits), lib=lib)
+    if not (np.all(r["out"] == 0) and np.all(np.isneginf(r["lse"]))):
+        fails.append("fully skipped row")
+    if not np.array_equal(bits_of(r["mask_out"], 2), bits):
+        fails.append("input marks lost")
+    return fails
+
+
+ALL_CHECKS = (run_golden, check_dense, check_masked_and_rule, check_tile_invariance, check_edge_cases)
