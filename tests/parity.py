@@ -1,0 +1,139 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+compare it with the CPU oracle on the same inputs.
+
+Comparison rules:
+  * outputs: max |gpu - oracle| <= 2e-2 for bf16 storage, 1e-5 for fp32;
+  * lse: <= 1e-3 (bf16 path, fp32 arithmetic) / 1e-5 (fp32 path), same -inf pattern;
+  * masks: bit-exact, except a tile whose oracle margin lies within 1e-3 of
+    tau (in natural-log units): either decision is accepted there, and such
+    tiles are counted.
+Inputs of the oracle never come from the HIP path: q/k/v come from the seeded
+generator, mask_in from the generator or from the oracle's own previous step.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+from oracle import oracle
+from temporal_block_sparse_amd import lite_attn as la
+
+TOL_OUT = {torch.bfloat16: 2e-2, torch.float32: 1e-5}
+TOL_LSE = {torch.bfloat16: 1e-3, torch.float32: 1e-5}
+NEAR_TAU = 1e-3
+
+
+def words_to_u32(m):
+    return np.asarray(m).view(np.uint32)
+
+
+def gpu_fwd(q, k, v, BM, BN, tau, scale, mask_in=None, mark=True, use_skiplist=False, inplace=False,
+            want_lse=True):
+    """Run the HIP forward on device copies of q, k, v (any device).  mask_in:
+    host or device words or None.  Returns (out, lse, mask_out) on the CPU
+    (mask_out None when mark is False)."""
+    dev = torch.device("cuda")
+    qd, kd, vd = (t.to(dev).contiguous() for t in (q, k, v))
+    desc = la.desc_of(qd, BM, BN)
+    nw = la.lite_attn_mask_words(desc)
+    mi = None
+    if mask_in is not None:
+        mi = torch.as_tensor(np.asarray(mask_in).view(np.int32).reshape(-1)).to(dev) if not isinstance(
+            mask_in, torch.Tensor) else mask_in.to(dev).view(torch.int32).reshape(-1).contiguous()
+        assert mi.numel() == nw
+    mo = None
+    if mark:
+        if inplace:
+            if mi is None:
+                mi = torch.zeros(nw, dtype=torch.int32, device=dev)
+            mo = mi
+        else:
+            mo = torch.full((nw,), 0x5A5A5A5A, dtype=torch.int32, device=dev)
+    sl = None
+    if use_skiplist:
+        sl = torch.full((la.lite_attn_skiplist_len(desc),), -7, dtype=torch.int32, device=dev)
+        la.lite_attn_build_skiplist(desc, mi, sl)
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full((qd.shape[0], qd.shape[2], qd.shape[1]), float("nan"), device=dev) if want_lse else None
+    la.lite_attn_fwd(qd, kd, vd, out, tile_m=BM, tile_n=BN, tau=tau, softmax_scale=scale, mask_in=mi,
+                     mask_out=mo, skiplist=sl, lse=lse)
+    torch.cuda.synchronize()
+    return (out.cpu(), lse.cpu() if lse is not None else None,
+            mo.cpu().numpy().view(np.uint32).reshape(-1, desc_words(desc)) if mo is not None else None)
+
+
+def desc_words(desc):
+    tk = -(-desc.seqlen // desc.tile_n)
+    return -(-tk // 32)
+
+
+def row_coords(row, H, Tq):
+    return int(row // (Tq * H)), int((row // Tq) % H), int(row % Tq)
+
+
+def compare_rows(gpu, orc, rows, B, N, H, BM, BN, tau, dtype, mask_checked=True):
+    """Compare GPU results (full tensors) with packed oracle rows.  Returns a
+    dict of error statistics; raises AssertionError on a violation."""
+    out_g, lse_g, mask_g = gpu
+    Tq, Tk = -(-N // BM), -(-N // BN)
+    W = -(-Tk // 32)
+    og = out_g.to(torch.float64).numpy()
+    lg = lse_g.numpy().astype(np.float64) if lse_g is not None else None
+    max_out = 0.0
+    max_lse = 0.0
+    near, mism = 0, 0
+    for i, row in enumerate(rows):
+        b, h, qt = row_coords(row, H, Tq)
+        r0, nr = qt * BM, min(BM, N - qt * BM)
+        ref = orc["out"][i][:nr]
+        got = og[b, r0:r0 + nr, h, :]
+        assert np.all(np.isfinite(got)), "non-finite output in row %d" % row
+        max_out = max(max_out, float(np.abs(got - ref).max()))
+        if lg is not None:
+            lr, lgot = orc["lse"][i][:nr], lg[b, h, r0:r0 + nr]
+            assert np.array_equal(np.isneginf(lr), np.isneginf(lgot)), "lse -inf pattern, row %d" % row
+            fin = np.isfinite(lr)
+            if fin.any():
+                max_lse = max(max_lse, float(np.abs(lgot[fin] - lr[fin]).max()))
+        if mask_checked and mask_g is not None:
+            mw = mask_g[row]
+            mo = orc["mask_out"][i]
+            diff = mw ^ mo
+            for kt in range(Tk):
+                if (int(diff[kt // 32]) >> (kt % 32)) & 1:
+                    mg = orc["margin"][i][kt]
+                    if np.isfinite(mg) and abs(mg - tau) <= NEAR_TAU:
+                        near += 1
+                    else:
+                        mism += 1
+            # padding bits must be zero
+            if Tk % 32:
+                assert (int(mw[W - 1]) >> (Tk % 32)) == 0, "padding bits set, row %d" % row
+    stats = dict(max_out=max_out, max_lse=max_lse, near_tau=near, mask_mismatch=mism)
+    assert max_out <= TOL_OUT[dtype], stats
+    assert max_lse <= TOL_LSE[dtype], stats
+    assert mism == 0, stats
+    return stats
+
+
+def check_full(q, k, v, BM, BN, tau, scale, mask_in=None, use_skiplist=False, nthreads=None):
+    """All rows: GPU vs oracle.  Returns (stats, oracle result)."""
+    B, N, H, D = q.shape
+    orc = oracle.fwd(q, k, v, BM, BN, tau, scale, mask_in=mask_in, nthreads=nthreads)
+    gpu = gpu_fwd(q, k, v, BM, BN, tau, scale, mask_in=mask_in, use_skiplist=use_skiplist)
+    stats = compare_rows(gpu, orc, orc["rows"], B, N, H, BM, BN, tau, q.dtype)
+    return stats, orc
+
+
+def sample_rows(B, H, Tq, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    rows.add((B * H - 1) * Tq + Tq - 1)          # last head's last (partial) q-tile
+    rows.add(0)
+    rows.add(Tq - 1)
+    if B > 1:
+        rows.add((H * Tq) + Tq // 2)             # second batch entry
+    while len(rows) < n:
+        rows.add(int(rng.integers(0, B * H * Tq)))
+    return np.array(sorted(rows), np.int64)

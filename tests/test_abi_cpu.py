@@ -1,0 +1,139 @@
+"""The C-ABI library loads, exports every declared symbol and validates its
+arguments on the host.  No kernel is launched: every call here is rejected
+(or is an empty no-op) before the library touches the device."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from temporal_block_sparse_amd import lite_attn as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lite_attn.h")
+
+BF16 = dict(batch=1, seqlen=1000, heads=2, head_dim=128, tile_m=128, tile_n=128, dtype=la.LITE_BF16)
+FAKE = 1 << 40  # an address that is never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lite_attn_\w+)\s*\(", src)))
+
+
+def desc(**kw):
+    d = dict(BF16)
+    d.update(kw)
+    return la.Desc(d["batch"], d["seqlen"], d["heads"], d["head_dim"], d["tile_m"], d["tile_n"], d["dtype"])
+
+
+def fwd(d, q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), mask_in=None, mask_out=None, skiplist=None,
+        tau=-3.0, scale=0.125, out=FAKE + (3 << 30), lse=None):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return la.LIB.lite_attn_fwd(ctypes.byref(d) if d is not None else None, P(q), P(k), P(v), P(mask_in),
+                                P(mask_out), P(skiplist), tau, scale, P(out), P(lse), None)
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(la.EXPORTS) <= set(names) and len(names) == len(la.EXPORTS)
+    lib = ctypes.CDLL(la.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert la.LIB.lite_attn_abi_version() == 1
+
+
+def test_sizes():
+    d = desc()
+    tq, tk = 8, 8
+    assert la.lite_attn_mask_words(d) == 1 * 2 * tq * 1
+    assert la.lite_attn_skiplist_len(d) == 1 * 2 * tq * (1 + tk)
+    d = desc(seqlen=75600, heads=40)
+    assert la.lite_attn_mask_words(d) == 40 * 591 * 19
+    assert la.lite_attn_skiplist_len(d) == 40 * 591 * 592
+    assert la.lite_attn_mask_words(desc(seqlen=-1)) == 0
+
+
+def test_strerror_covers_every_code():
+    for code in range(0, 9):
+        assert la.lite_attn_strerror(code)
+    assert "unknown" in la.lite_attn_strerror(1234)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(seqlen=-1), 2), (dict(batch=-2), 2), (dict(head_dim=0), 2), (dict(tile_n=0), 2),
+    (dict(head_dim=96), 3), (dict(tile_m=64), 3), (dict(tile_n=32), 3), (dict(dtype=7), 3),
+    (dict(dtype=la.LITE_FP32), 3), (dict(dtype=la.LITE_FP32, head_dim=64, tile_m=64, tile_n=32), 3),
+    (dict(seqlen=4097 * 128), 3),
+])
+def test_descriptor_errors(kw, code):
+    assert fwd(desc(**kw)) == code
+
+
+def test_null_arguments():
+    assert fwd(None) == 1
+    assert fwd(desc(), q=None) == 1
+    assert fwd(desc(), out=None) == 1
+    assert la.LIB.lite_attn_build_skiplist(ctypes.byref(desc()), None, None, None) == 1
+    assert la.LIB.lite_attn_reset_mask(ctypes.byref(desc()), None, None) == 1
+
+
+def test_threshold_rules(monkeypatch):
+    assert fwd(desc(), tau=float("nan")) == 4
+    monkeypatch.delenv("LITE_ATTENTION_DEBUG", raising=False)
+    assert fwd(desc(), tau=0.5) == 4
+    monkeypatch.setenv("LITE_ATTENTION_DEBUG", "FALSE")
+    assert fwd(desc(), tau=0.5) == 4
+    monkeypatch.setenv("LITE_ATTENTION_DEBUG", "1")
+    assert fwd(desc(), tau=0.5, q=None) == 1           # threshold accepted, then the NULL q is reported
+    assert fwd(desc(), tau=0.0, q=None) == 1
+    assert fwd(desc(), tau=-math.inf, q=None) == 1
+
+
+def test_scale_rules():
+    for s in (0.0, -1.0, float("inf"), float("nan")):
+        assert fwd(desc(), scale=s) == 5
+
+
+def test_alignment():
+    assert fwd(desc(), q=FAKE + 8) == 6
+    assert fwd(desc(), out=FAKE + (3 << 30) + 2) == 6
+    assert fwd(desc(), mask_in=FAKE + (5 << 30) + 1) == 6
+    assert fwd(desc(), lse=FAKE + (6 << 30) + 2) == 6
+
+
+def test_aliasing():
+    assert fwd(desc(), out=FAKE) == 7                                   # out is q
+    assert fwd(desc(), out=FAKE + 4096) == 7                            # out overlaps q
+    assert fwd(desc(), lse=FAKE + (2 << 30) + 64) == 7                  # lse inside v
+    m = FAKE + (5 << 30)
+    assert fwd(desc(), mask_in=m, mask_out=m + 4, q=None) == 1          # partial overlap is checked after NULL
+    assert fwd(desc(), mask_in=m, mask_out=m + 4) == 7
+    assert fwd(desc(), mask_in=m, mask_out=m, skiplist=m + 32) == 7      # mask_out overlaps the skip-list
+
+
+def test_empty_descriptor_is_a_noop():
+    for kw in (dict(seqlen=0), dict(batch=0), dict(heads=0)):
+        assert fwd(desc(**kw), q=None, k=None, v=None, out=None) == 0
+        assert la.LIB.lite_attn_reset_mask(ctypes.byref(desc(**kw)), None, None) == 0
+        assert la.LIB.lite_attn_build_skiplist(ctypes.byref(desc(**kw)), None, None, None) == 0
+    # an empty call still rejects a bad threshold or scale
+    assert fwd(desc(seqlen=0), tau=float("nan")) == 4
+
+
+def test_skiplist_and_reset_validation():
+    d = desc()
+    m = FAKE
+    assert la.LIB.lite_attn_build_skiplist(ctypes.byref(d), ctypes.c_void_p(m), ctypes.c_void_p(m + 2), None) == 6
+    assert la.LIB.lite_attn_build_skiplist(ctypes.byref(d), ctypes.c_void_p(m), ctypes.c_void_p(m + 8), None) == 7
+    assert la.LIB.lite_attn_reset_mask(ctypes.byref(d), ctypes.c_void_p(m + 1), None) == 6
+    assert la.LIB.lite_attn_reset_mask(ctypes.byref(desc(tile_m=-3)), ctypes.c_void_p(m), None) == 2
+
+
+def test_binding_raises_with_code():
+    with pytest.raises(la.LiteAttnError) as ei:
+        la._check(3)
+    assert ei.value.code == 3

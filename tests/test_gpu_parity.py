@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: outputs within 2e-2 max-abs (bf16 storage, fp32 accumulation) and 1e-5
+(fp32 storage); Skip-Mask decisions bit-exact except tiles whose oracle margin
+is within 1e-3 of the threshold (counted).  Inputs are the seeded synthetic
+video-token trajectories; every mask_in comes from the generator or from the
+oracle's own previous step.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from temporal_block_sparse_amd import configs, synth
+from temporal_block_sparse_amd import lite_attn as la
+from tests import parity as pa
+
+pytestmark = pytest.mark.gpu
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def small_wl(base, grid, heads, batch=1, steps=3):
+    return configs.scaled(base, grid, heads=heads, batch=batch, steps=steps)
+
+
+def run_trajectory(wl, steps, use_skiplist=False, nthreads=None):
+    """Oracle trajectory from an empty mask; at each step the GPU gets the same
+    inputs and the oracle's mask_in, and must match out, lse and mask_out."""
+    tr = synth.Trajectory(wl, "cpu")
+    mask = np.zeros((wl.rows, wl.mask_words), np.uint32)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    all_stats = []
+    for step in range(steps):
+        if step:
+            tr.advance()
+        q, k, v = tr.tensors()
+        tau = wl.tau_at(step)
+        log("  %s step %d tau %g" % (wl.name, step, tau))
+        stats, orc = pa.check_full(q, k, v, wl.tile_m, wl.tile_n, tau, scale, mask_in=mask,
+                                   use_skiplist=use_skiplist, nthreads=nthreads)
+        stats["sparsity"] = float(np.unpackbits(orc["mask_out"].view(np.uint8)).sum()) / (wl.rows * wl.tk)
+        all_stats.append(stats)
+        mask = orc["mask_out"]
+    return all_stats
+
+
+def test_c1_fp32_trajectory():
+    stats = run_trajectory(configs.C1, configs.C1.steps)
+    log("C1", stats)
+    assert stats[-1]["sparsity"] > 0.05
+
+
+@pytest.mark.parametrize("D,BN", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_bf16_ragged_shapes_trajectory(D, BN):
+    # 1000 tokens (5x10x20 grid): 8 q-tiles, the last holding 104 queries; the
+    # last k-tile holds 104 (BN=128) or 40 (BN=64) keys.  At head_dim 128 the
+    # positional bias is raised to 6 so that this short sequence marks tiles.
+    base = configs.C3 if D == 128 else configs.C2
+    wl = configs.Workload(**{**base.__dict__, "name": "ragged", "grid": (5, 10, 20), "heads": 3, "batch": 2,
+                             "head_dim": D, "tile_m": 128, "tile_n": BN,
+                             "bias_scale": (6.0, 6.0) if D == 128 else base.bias_scale})
+    stats = run_trajectory(wl, 3)
+    log("ragged", D, BN, stats)
+    assert stats[-1]["sparsity"] > 0.0
+
+
+def test_c2_trajectory_full_shape():
+    wl = configs.C2
+    stats = run_trajectory(wl, 4)
+    log("C2", stats)
+    assert stats[-1]["sparsity"] > 0.05
+
+
+def test_c2_trajectory_skiplist_path():
+    wl = configs.scaled(configs.C2, configs.C2.grid, heads=3, steps=6)
+    stats = run_trajectory(wl, wl.steps, use_skiplist=True)
+    log("C2 skiplist", stats)
+
+
+def test_skiplist_path_bit_identical_to_bitmask():
+    wl = small_wl(configs.C3, (6, 10, 20), heads=4, batch=2)
+    q, k, v = synth.Trajectory(wl, "cpu").tensors()
+    mask = synth.random_mask(wl.rows, wl.tk, 0.4, seed=3).numpy()
+    a = pa.gpu_fwd(q, k, v, 128, 128, -3.0, 0.088, mask_in=mask)
+    b = pa.gpu_fwd(q, k, v, 128, 128, -3.0, 0.088, mask_in=mask, use_skiplist=True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+
+
+def test_mask_updated_in_place_equals_separate_buffers():
+    wl = small_wl(configs.C2, (4, 16, 16), heads=2)
+    q, k, v = synth.Trajectory(wl, "cpu").tensors()
+    mask = synth.random_mask(wl.rows, wl.tk, 0.2, seed=4).numpy()
+    a = pa.gpu_fwd(q, k, v, 128, 64, -3.0, 0.125, mask_in=mask)
+    b = pa.gpu_fwd(q, k, v, 128, 64, -3.0, 0.125, mask_in=mask, inplace=True)
+    assert torch.equal(a[0], b[0]) and np.array_equal(a[2], b[2])
+
+
+def test_null_masks_and_minus_inf_threshold():
+    wl = small_wl(configs.C2, (4, 16, 16), heads=2)
+    q, k, v = synth.Trajectory(wl, "cpu").tensors()
+    zeros = np.zeros((wl.rows, wl.mask_words), np.uint32)
+    a = pa.gpu_fwd(q, k, v, 128, 64, -3.0, 0.125, mask_in=None)
+    b = pa.gpu_fwd(q, k, v, 128, 64, -3.0, 0.125, mask_in=zeros)
+    c = pa.gpu_fwd(q, k, v, 128, 64, -3.0, 0.125, mask_in=None, mark=False)
+    d = pa.gpu_fwd(q, k, v, 128, 64, -math.inf, 0.125, mask_in=None)
+    assert torch.equal(a[0], b[0]) and np.array_equal(a[2], b[2])
+    assert torch.equal(a[0], c[0]) and c[2] is None
+    assert torch.equal(a[0], d[0]) and not d[2].any()
+    orc = oracle.fwd(q, k, v, 128, 64, -math.inf, 0.125)
+    pa.compare_rows(d, orc, orc["rows"], 1, wl.seqlen, 2, 128, 64, -math.inf, torch.bfloat16)
+
+
+def test_fully_skipped_rows_give_zero():
+    wl = small_wl(configs.C2, (4, 16, 16), heads=2)
+    q, k, v = synth.Trajectory(wl, "cpu").tensors()
+    mask = synth.random_mask(wl.rows, wl.tk, 0.3, seed=5).numpy()
+    mask[1, :] = -1                  # every tile of row 1 skipped (padding bits too: ignored)
+    out, lse, mo = pa.gpu_fwd(q, k, v, 128, 64, -3.0, 0.125, mask_in=mask)
+    b, h, qt = pa.row_coords(1, 2, wl.tq)
+    assert torch.all(out[b, qt * 128:(qt + 1) * 128, h] == 0)
+    assert torch.all(torch.isneginf(lse[b, h, qt * 128:(qt + 1) * 128]))
+    orc = oracle.fwd(q, k, v, 128, 64, -3.0, 0.125, mask_in=mask)
+    pa.compare_rows((out, lse, mo), orc, orc["rows"], 1, wl.seqlen, 2, 128, 64, -3.0, torch.bfloat16)
+
+
+@pytest.mark.parametrize("tk", [1, 5, 31, 32, 33, 64, 65, 200, 591])
+def test_build_skiplist_matches_reference(tk):
+    rows = 37
+    desc = la.make_desc(1, tk * 128, rows, 128, tk * 128, 128, la.LITE_BF16)   # one q-tile per head
+    mask = synth.random_mask(rows, tk, 0.5, seed=tk)
+    mask[3] = 0                                                          # all live
+    mask[4] = -1                                                         # all skipped
+    sl = torch.full((la.lite_attn_skiplist_len(desc),), -9, dtype=torch.int32, device="cuda")
+    la.lite_attn_build_skiplist(desc, mask.cuda().reshape(-1), sl)
+    got = sl.cpu().numpy().reshape(rows, 1 + tk)
+    counts, lists = oracle.skiplist(mask.numpy(), tk)
+    for r in range(rows):
+        assert got[r, 0] == counts[r]
+        assert list(got[r, 1:1 + counts[r]]) == list(lists[r])
+
+
+def test_reset_mask_clears_every_word():
+    desc = la.make_desc(2, 5000, 3, 128, 128, 128, la.LITE_BF16)
+    m = torch.full((la.lite_attn_mask_words(desc) + 8,), -1, dtype=torch.int32, device="cuda")
+    la.lite_attn_reset_mask(desc, m[:-8])
+    torch.cuda.synchronize()
+    assert int(m[:-8].abs().sum()) == 0 and bool((m[-8:] == -1).all())
+
+
+@pytest.mark.parametrize("N", [1, 7, 64, 127, 128, 129, 300])
+def test_edge_sequence_lengths(N):
+    for D, BN in ((64, 64), (128, 128)):
+        q, k, v = synth.random_qkv(1, N, 2, D, torch.bfloat16, seed=N, scale=2.0)
+        pa.check_full(q, k, v, 128, BN, -1.0, 1.0 / math.sqrt(D))
+    q, k, v = synth.random_qkv(1, N, 2, 64, torch.float32, seed=N, scale=2.0)
+    pa.check_full(q, k, v, 64, 64, -1.0, 0.125)
+
+
+def test_empty_sequence_is_noop():
+    q = torch.empty(1, 0, 2, 128, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    la.lite_attn_fwd(q, q.clone(), q.clone(), out, tile_m=128, tile_n=128, tau=-3.0)
+
+
+def test_maximum_k_tiles():
+    """Tk = 4096 (524,288 tokens, 128 mask words per row) with 95% of tiles skipped."""
+    N, H, D = 4096 * 128, 1, 128
+    q, k, v = synth.random_qkv(1, N, H, D, torch.bfloat16, seed=1, scale=1.0, device="cuda")
+    Tq = N // 128
+    mask = synth.random_mask(H * Tq, 4096, 0.95, seed=11).numpy()
+    rows = np.array([0, Tq // 2, Tq - 1], np.int64)
+    gpu = pa.gpu_fwd(q, k, v, 128, 128, -3.0, 0.088, mask_in=mask)
+    orc = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), 128, 128, -3.0, 0.088, mask_in=mask, rows=rows)
+    pa.compare_rows(gpu, orc, rows, 1, N, H, 128, 128, -3.0, torch.bfloat16)
+
+
+@pytest.mark.parametrize("name", ["c3_bf16_33k", "c4_bf16_76k", "c5_bf16_76k_pair"])
+def test_full_size_sampled_rows(name):
+    """Full-size workloads in the benchmark's launch configuration: step 0 (empty
+    mask) and a step from a synthetic 60%-sparse mask, on sampled rows."""
+    wl = configs.ALL[name]
+    tr = synth.Trajectory(wl, "cuda")
+    q, k, v = tr.tensors()
+    del tr
+    torch.cuda.empty_cache()
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    tau = wl.tau_at(0, -3.0)
+    rows = pa.sample_rows(wl.batch, wl.heads, wl.tq, 10, seed=7)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    for case, mask in (("empty", None), ("synthetic", synth.random_mask(wl.rows, wl.tk, 0.6, seed=8).numpy())):
+        log("  %s %s tau %g rows %s" % (name, case, tau, rows.tolist()))
+        gpu = pa.gpu_fwd(q, k, v, wl.tile_m, wl.tile_n, tau, scale, mask_in=mask,
+                         use_skiplist=(wl.batch == 2))
+        orc = oracle.fwd(qc, kc, vc, wl.tile_m, wl.tile_n, tau, scale, mask_in=mask, rows=rows)
+        st = pa.compare_rows(gpu, orc, rows, wl.batch, wl.seqlen, wl.heads, wl.tile_m, wl.tile_n, tau,
+                             torch.bfloat16)
+        log("  ", st)
