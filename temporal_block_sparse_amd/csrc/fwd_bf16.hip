@@ -1,6 +1,7 @@
 // Skip-masked tiled attention forward, bf16 in / bf16 out, fp32 accumulation,
 // hand-written for gfx950 (CDNA4): one workgroup of 4 wave64s per
-// (batch, head, q-tile of 128 queries); each wave owns 32 queries.
+// (batch, head, q-tile of 128 queries); each wave owns 32 queries; two
+// workgroups share a CU.
 //
 // Method (LiteAttention README, "QK-Skip Algorithm" and "Full-Stage
 // Elimination"; arXiv 2511.11062 abstract): k-tiles set in the Skip-Mask are
@@ -17,15 +18,23 @@
 //   single query (lane % 32): its row max needs only in-register max plus one
 //   v_permlane32_swap with the other half-wave, P^T feeds the second MFMA
 //   straight from registers, and the O rescale uses the lane's own factor.
-// * K tile rows are stored in LDS with rows 4..7 and 8..11 of every 16 swapped,
-//   so that the 8 scores a lane holds per 16-key step are 8 consecutive keys;
-//   V is stored transposed (V^T, e-major) so the PV A-operand is one 16-byte
-//   LDS read.  Its rows are permuted so a lane's O^T values are 16
-//   consecutive head-dim entries (two 16-byte global stores).
+// * A k-tile is consumed in steps of 64 keys.  The online softmax is updated
+//   per step (exact in any grouping); the QK-Skip test uses the maximum over
+//   all steps of the tile against the running max taken before its first step.
+// * Two 64-key steps are double-buffered in LDS (64 KB at head_dim 128), so
+//   two workgroups fit on a CU and each SIMD interleaves two waves: one wave's
+//   softmax (VALU, v_exp) runs under the other's MFMAs.  The next step's
+//   global loads are issued before the current step's MFMAs and land in the
+//   other buffer afterwards; one barrier per step.
+// * K rows are stored in LDS with rows 4..7 and 8..11 of every 16 swapped, so
+//   that the 8 scores a lane holds per 16-key MFMA step are 8 consecutive
+//   keys; V is stored transposed (V^T, e-major) via an in-register 4x8
+//   transpose (v_perm_b32), so the PV A-operand is one 16-byte LDS read, with
+//   its rows permuted so a lane's O^T values are 16 consecutive head-dim
+//   entries (two 16-byte global stores).
 // * 16-byte chunks are XOR-swizzled per row against LDS bank conflicts.
-// * K/V tiles are double-buffered in LDS; the next live tile's global loads
-//   are issued before the current tile's MFMAs and land in the other buffer
-//   afterwards; one barrier per tile.
+// * Loads use a wave-uniform tile base plus a per-lane 32-bit offset fixed for
+//   the whole kernel; only the ragged last tile takes the predicated path.
 // * The QK-Skip vote is one ballot per wave and tile; a wave that wants to
 //   keep the tile sets its bit in an LDS keep-vector with one atomic OR.  The
 //   mask row is written once, in the epilogue.
@@ -41,20 +50,22 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 128;       // queries per workgroup (one q-tile)
 constexpr int NWAVES = 4;
 constexpr int NT = 64 * NWAVES;
+constexpr int HK = 64;        // keys per step
 constexpr int MAXW = 128;     // mask words per row (Tk <= 4096)
 
-// LDS row r of a K tile holds key kperm(r): rows 4..7 and 8..11 of each 16 swapped.
+// LDS row r of a K step holds key kperm(r): rows 4..7 and 8..11 of each 16 swapped.
 __device__ __forceinline__ int kperm(int r)
 {
     const int m = r & 15;
     return (m >= 4 && m < 8) ? r + 4 : ((m >= 8 && m < 12) ? r - 4 : r);
 }
 
-// LDS row of head-dim entry e in a V^T tile: within each 32-block,
+// LDS row of head-dim entry e in a V^T step: within each 32-block,
 // e = 16*g + 4*a + b is stored at row 8*a + 4*g + b.
 __device__ __forceinline__ int vt_row(int e)
 {
@@ -129,25 +140,22 @@ struct LiveTiles {
     }
 };
 
-template <int D, int BN>
-struct Tile {
-    static constexpr int KCHUNKS = BN * D / 8;          // 16-byte chunks of a K tile
-    static constexpr int VCHUNKS = BN * D / 8;          // of a V^T tile
-    static constexpr int STAGE = KCHUNKS + VCHUNKS;
-    static constexpr int KPT = KCHUNKS / NT;            // K chunks per thread
-    static constexpr int VBLK = BN * D / 64;            // 8x8 V blocks
-    static constexpr int WAVES_PER_EU = (BN * D <= 64 * 64) ? 2 : 1;
-    static_assert(KCHUNKS % NT == 0, "tile too small");
-    static_assert(VBLK <= NT, "tile too large");
+template <int D>
+struct Geo {
+    static constexpr int KCH = HK * D / 8;   // 16-byte chunks of a K step (= of a V^T step)
+    static constexpr int STAGE = 2 * KCH;    // K then V^T, in 16-byte chunks
+    static constexpr int KPT = KCH / NT;     // K chunks per thread
+    static constexpr int VK = HK * D / 8 / NT;  // keys per thread's V block (VK x 8 head-dim entries)
+    static_assert(KCH % NT == 0 && (VK == 2 || VK == 4), "unsupported step geometry");
 };
 
 template <int D, int BN>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT),
-                               amdgpu_waves_per_eu(Tile<D, BN>::WAVES_PER_EU, Tile<D, BN>::WAVES_PER_EU)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(FwdParams p, float c2, float tau2)
 {
-    using T = Tile<D, BN>;
-    __shared__ u32x4 smem[2 * T::STAGE];
+    using G = Geo<D>;
+    constexpr int SPT = BN / HK;  // steps per k-tile
+    __shared__ u32x4 smem[2 * G::STAGE];
     __shared__ uint32_t keep[MAXW];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -157,11 +165,11 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     const int qt = (int)(row % Tq);
     const int64_t bh = row / Tq;
     const int h = (int)(bh % H), b = (int)(bh / H);
-    const int64_t rs = (int64_t)H * D;  // token stride (elements)
+    const int rs = H * D;  // token stride (elements)
     const int64_t base = (int64_t)b * N * rs + (int64_t)h * D;
     const __bf16 *Qb = (const __bf16 *)p.q + base;
-    const __bf16 *Kb = (const __bf16 *)p.k + base;
-    const __bf16 *Vb = (const __bf16 *)p.v + base;
+    const char *Kb = (const char *)((const __bf16 *)p.k + base);
+    const char *Vb = (const char *)((const __bf16 *)p.v + base);
     const uint32_t *mrow = p.mask_in ? p.mask_in + row * W : nullptr;
     const bool vote = p.mask_out != nullptr;
 
@@ -180,53 +188,63 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         qf[ds] = __builtin_bit_cast(bf16x8, x);
     }
 
-    u32x4 kreg[T::KPT];
-    u32x4 vreg[8];
-    auto load_tile = [&](int kt) {
-        const int key0 = kt * BN;
+    // per-thread load slots (fixed for the kernel): K chunk i is key row kr[i],
+    // 16-byte column kc[i]; V block j covers keys 4*vk[j]..+3, head-dim 8*vc..+7
+    int koff[G::KPT], kr[G::KPT], klds[G::KPT];
 #pragma unroll
-        for (int i = 0; i < T::KPT; ++i) {
-            const int C = tid + i * NT, r = C / (D / 8), c = C % (D / 8);
-            const int key = key0 + r;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (key < N)
-                x = *(const u32x4 *)(Kb + (int64_t)key * rs + c * 8);
-            kreg[i] = x;
-        }
-        if (tid < T::VBLK) {
-            const int c = tid % (D / 8), kg = tid / (D / 8);
+    for (int i = 0; i < G::KPT; ++i) {
+        const int C = tid + i * NT, r = C / (D / 8), c = C % (D / 8);
+        kr[i] = r;
+        koff[i] = r * rs * 2 + c * 16;
+        const int lr = kperm(r);
+        klds[i] = lr * (D / 8) + (c ^ swz(lr));
+    }
+    const int vc = tid % (D / 8);              // V block: head-dim entries 8*vc..+7
+    const int vk = tid / (D / 8);              //          keys VK*vk..+VK-1 of the step
+    const int voff = vk * G::VK * rs * 2 + vc * 16;
+
+    u32x4 kreg[G::KPT];
+    u32x4 vreg[G::VK];
+    auto load_step = [&](int key0) {
+        const char *kb = Kb + (int64_t)key0 * rs * 2;
+        const char *vb = Vb + (int64_t)key0 * rs * 2;
+        if (key0 + HK <= N) {
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int key = key0 + kg * 8 + r;
-                u32x4 x = {0u, 0u, 0u, 0u};
-                if (key < N)
-                    x = *(const u32x4 *)(Vb + (int64_t)key * rs + c * 8);
-                vreg[r] = x;
-            }
+            for (int i = 0; i < G::KPT; ++i)
+                kreg[i] = *(const u32x4 *)(kb + koff[i]);
+#pragma unroll
+            for (int r = 0; r < G::VK; ++r)
+                vreg[r] = *(const u32x4 *)(vb + voff + r * rs * 2);
+        } else {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int i = 0; i < G::KPT; ++i)
+                kreg[i] = (key0 + kr[i] < N) ? *(const u32x4 *)(kb + koff[i]) : z;
+#pragma unroll
+            for (int r = 0; r < G::VK; ++r)
+                vreg[r] = (key0 + G::VK * vk + r < N) ? *(const u32x4 *)(vb + voff + r * rs * 2) : z;
         }
     };
-    auto store_tile = [&](int stage) {
-        u32x4 *Ks = smem + stage * T::STAGE;
-        u32x4 *Vs = Ks + T::KCHUNKS;
+    auto store_step = [&](int stage) {
+        u32x4 *Ks = smem + stage * G::STAGE;
+        char *Vs = (char *)(Ks + G::KCH);
 #pragma unroll
-        for (int i = 0; i < T::KPT; ++i) {
-            const int C = tid + i * NT, r = C / (D / 8), c = C % (D / 8);
-            const int lr = kperm(r);
-            Ks[lr * (D / 8) + (c ^ swz(lr))] = kreg[i];
-        }
-        if (tid < T::VBLK) {
-            const int c = tid % (D / 8), kg = tid / (D / 8);
+        for (int i = 0; i < G::KPT; ++i)
+            Ks[klds[i]] = kreg[i];
+        // VK keys x 8 head-dim entries -> 8 rows of V^T holding VK keys (2*VK bytes) each
+        constexpr int PER_CHUNK = 8 / G::VK;    // key groups per 16-byte chunk
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                // column j of the 8x8 block (8 keys of head-dim entry c*8 + j)
-                u32x4 o;
-#pragma unroll
-                for (int pr = 0; pr < 4; ++pr) {
-                    const uint32_t lo = vreg[2 * pr][j >> 1], hi = vreg[2 * pr + 1][j >> 1];
-                    o[pr] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-                }
-                const int lr = vt_row(c * 8 + j);
-                Vs[lr * (BN / 8) + (kg ^ swz(lr))] = o;
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            const int lr = vt_row(vc * 8 + e);
+            char *dst = Vs + (lr * (HK / 8) + ((vk / PER_CHUNK) ^ swz(lr))) * 16 + (vk % PER_CHUNK) * 2 * G::VK;
+            if constexpr (G::VK == 4) {
+                u32x2 o;
+                o[0] = __builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel);
+                o[1] = __builtin_amdgcn_perm(vreg[3][e >> 1], vreg[2][e >> 1], sel);
+                *(u32x2 *)dst = o;
+            } else {
+                *(uint32_t *)dst = __builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel);
             }
         }
     };
@@ -238,108 +256,128 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         for (int v = 0; v < 16; ++v)
             O[eb][v] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
+    float m_before = -INFINITY, m_tile = -INFINITY;
 
     LiveTiles it;
     it.init(mrow, p.skiplist ? p.skiplist + row * (1 + Tk) : nullptr, Tk);
     int kt = it.next();
+    int sub = 0;
     if (kt >= 0) {
-        load_tile(kt);
-        store_tile(0);
+        load_step(kt * BN);
+        store_step(0);
     }
     __syncthreads();
-    int kt_next = kt >= 0 ? it.next() : -1;
+    int kt_after = kt >= 0 ? it.next() : -1;  // next live tile after kt
     int stage = 0;
 
     while (kt >= 0) {
-        if (kt_next >= 0)
-            load_tile(kt_next);
+        // the step after this one
+        int kt_n = kt, sub_n = sub + 1;
+        if (sub_n == SPT) {
+            kt_n = kt_after;
+            sub_n = 0;
+        }
+        const int key0 = kt * BN + sub * HK;
+        if (kt_n >= 0 && kt_n * BN + sub_n * HK < N)
+            load_step(kt_n * BN + sub_n * HK);
 
-        const u32x4 *Ks = smem + stage * T::STAGE;
-        const u32x4 *Vs = Ks + T::KCHUNKS;
+        const u32x4 *Ks = smem + stage * G::STAGE;
+        const u32x4 *Vs = Ks + G::KCH;
+        if (sub == 0) {
+            m_before = m_run;
+            m_tile = -INFINITY;
+        }
 
-        // ---- S^T = K Q^T (raw logits, fp32) ----
-        f32x16 S[BN / 32];
+        if (key0 < N) {
+            // ---- S^T = K Q^T (raw logits, fp32) ----
+            f32x16 S[HK / 32];
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
+            for (int kb = 0; kb < HK / 32; ++kb) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                S[kb][v] = 0.f;
-            const int lr = kb * 32 + lq;
+                for (int v = 0; v < 16; ++v)
+                    S[kb][v] = 0.f;
+                const int lr = kb * 32 + lq;
 #pragma unroll
-            for (int ds = 0; ds < D / 16; ++ds) {
-                const u32x4 a = Ks[lr * (D / 8) + ((2 * ds + g) ^ swz(lr))];
-                S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ds], S[kb],
-                                                                0, 0, 0);
+                for (int ds = 0; ds < D / 16; ++ds) {
+                    const u32x4 a = Ks[lr * (D / 8) + ((2 * ds + g) ^ swz(lr))];
+                    S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ds], S[kb],
+                                                                    0, 0, 0);
+                }
+            }
+
+            // keys past the end of the sequence do not exist
+            if (key0 + HK > N) {
+#pragma unroll
+                for (int kb = 0; kb < HK / 32; ++kb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (key0 + kb * 32 + 16 * (v >> 3) + 8 * g + (v & 7) >= N)
+                            S[kb][v] = -INFINITY;
+            }
+
+            // ---- step-local max (log2 units) ----
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < HK / 32; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    mx = fmaxf(mx, S[kb][v]);
+            mx = fmaxf(mx, other_half(mx));
+            const float m_loc = mx * c2;
+            m_tile = fmaxf(m_tile, m_loc);
+
+            // ---- online softmax ----
+            const float m_new = fmaxf(m_run, m_loc);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            const float neg = -m_new;
+            float rsum = 0.f;
+            bf16x8 P[HK / 16];
+#pragma unroll
+            for (int kb = 0; kb < HK / 32; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][v], c2, neg));
+                    rsum += pv;
+                    P[kb * 2 + (v >> 3)][v & 7] = (__bf16)pv;
+                }
+            l_run = l_run * alpha + rsum;
+            m_run = m_new;
+            if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+                for (int eb = 0; eb < D / 32; ++eb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        O[eb][v] *= alpha;
+            }
+
+            // ---- O^T += V^T P^T ----
+#pragma unroll
+            for (int eb = 0; eb < D / 32; ++eb) {
+                const int lr = eb * 32 + lq;
+#pragma unroll
+                for (int ks = 0; ks < HK / 16; ++ks) {
+                    const u32x4 a = Vs[lr * (HK / 8) + ((2 * ks + g) ^ swz(lr))];
+                    O[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), P[ks], O[eb],
+                                                                    0, 0, 0);
+                }
             }
         }
 
-        // keys past the end of the sequence do not exist
-        const int key0 = kt * BN;
-        if (key0 + BN > N) {
-#pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    if (key0 + kb * 32 + 16 * (v >> 3) + 8 * g + (v & 7) >= N)
-                        S[kb][v] = -INFINITY;
-        }
-
-        // ---- tile-local max (log2 units), QK-Skip vote ----
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                mx = fmaxf(mx, S[kb][v]);
-        mx = fmaxf(mx, other_half(mx));
-        const float m_loc = mx * c2;
-        if (vote) {
-            const bool keep_lane = qvalid && !(m_loc - m_run < tau2);
+        // ---- QK-Skip vote once the whole tile has been seen ----
+        if (vote && sub == SPT - 1) {
+            const bool keep_lane = qvalid && !(m_tile - m_before < tau2);
             if (__ballot(keep_lane) != 0ull && lane == 0)
                 atomicOr(&keep[kt >> 5], 1u << (kt & 31));
         }
 
-        // ---- online softmax ----
-        const float m_new = fmaxf(m_run, m_loc);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        const float neg = -m_new;
-        float rsum = 0.f;
-        bf16x8 P[BN / 16];
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][v], c2, neg));
-                rsum += pv;
-                P[kb * 2 + (v >> 3)][v & 7] = (__bf16)pv;
-            }
-        l_run = l_run * alpha + rsum;
-        m_run = m_new;
-        if (__ballot(alpha != 1.0f) != 0ull) {
-#pragma unroll
-            for (int eb = 0; eb < D / 32; ++eb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    O[eb][v] *= alpha;
-        }
-
-        // ---- O^T += V^T P^T ----
-#pragma unroll
-        for (int eb = 0; eb < D / 32; ++eb) {
-            const int lr = eb * 32 + lq;
-#pragma unroll
-            for (int ks = 0; ks < BN / 16; ++ks) {
-                const u32x4 a = Vs[lr * (BN / 8) + ((2 * ks + g) ^ swz(lr))];
-                O[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), P[ks], O[eb], 0, 0,
-                                                                0);
-            }
-        }
-
-        if (kt_next >= 0)
-            store_tile(stage ^ 1);
+        if (kt_n >= 0 && kt_n * BN + sub_n * HK < N)
+            store_step(stage ^ 1);
         __syncthreads();
-        kt = kt_next;
-        kt_next = kt >= 0 ? it.next() : -1;
+        if (sub_n == 0) {
+            kt = kt_after;
+            kt_after = kt >= 0 ? it.next() : -1;
+        }
+        sub = sub_n;
         stage ^= 1;
     }
 
