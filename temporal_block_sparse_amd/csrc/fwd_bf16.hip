@@ -32,7 +32,7 @@
 //   transpose (v_perm_b32), so the PV A-operand is one 16-byte LDS read, with
 //   its rows permuted so a lane's O^T values are 16 consecutive head-dim
 //   entries (two 16-byte global stores).
-// * 16-byte chunks are XOR-swizzled per row against LDS bank conflicts.
+// * 16-byte LDS chunks are XOR-swizzled per row against bank conflicts.
 // * Loads use a wave-uniform tile base plus a per-lane 32-bit offset fixed for
 //   the whole kernel; only the ragged last tile takes the predicated path.
 // * The QK-Skip vote is one ballot per wave and tile; a wave that wants to
@@ -50,7 +50,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+#define LDS_S16X4(p) ((__attribute__((address_space(3))) s16x4 *)(p))
 
 constexpr int BM = 128;       // queries per workgroup (one q-tile)
 constexpr int NWAVES = 4;
@@ -64,19 +66,6 @@ __device__ __forceinline__ int kperm(int r)
     const int m = r & 15;
     return (m >= 4 && m < 8) ? r + 4 : ((m >= 8 && m < 12) ? r - 4 : r);
 }
-
-// LDS row of head-dim entry e in a V^T step: within each 32-block,
-// e = 16*g + 4*a + b is stored at row 8*a + 4*g + b.
-__device__ __forceinline__ int vt_row(int e)
-{
-    const int x = e & 31;
-    return (e & ~31) | (((x >> 2) & 3) << 3) | ((x >> 4) << 2) | (x & 3);
-}
-
-// 16-byte chunk swizzle: a bijection on the low 3 chunk bits for any 8
-// consecutive rows, and across rows that differ in bits 2, 4, 5 (the V^T
-// store pattern).
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 4) & 3); }
 
 __device__ __forceinline__ float other_half(float x)
 {
@@ -140,13 +129,25 @@ struct LiveTiles {
     }
 };
 
+// LDS layout of one 64-key step.
+// K: row-major (key x head-dim) with the kperm row order, rows padded by one
+//    16-byte chunk; the 16-byte MFMA A-operand reads of 32 consecutive rows
+//    are then free of bank conflicts.
+// V: row-major (key x head-dim), natural row order, rows padded by 64 bytes.
+//    The PV A-operand (V^T: 8 consecutive keys of one head-dim entry per lane)
+//    is read with ds_read_b64_tr_b16: in each 16-lane group, lane 4a+b points
+//    at 4 head-dim entries of key row a, and the hardware hands lane i the
+//    entries of column i for the 4 rows.  The 64-byte pad puts those 4 rows
+//    in different banks.
 template <int D>
 struct Geo {
-    static constexpr int KCH = HK * D / 8;   // 16-byte chunks of a K step (= of a V^T step)
-    static constexpr int STAGE = 2 * KCH;    // K then V^T, in 16-byte chunks
-    static constexpr int KPT = KCH / NT;     // K chunks per thread
-    static constexpr int VK = HK * D / 8 / NT;  // keys per thread's V block (VK x 8 head-dim entries)
-    static_assert(KCH % NT == 0 && (VK == 2 || VK == 4), "unsupported step geometry");
+    static constexpr int CH = HK * D / 8;       // 16-byte chunks of a K (or V) step
+    static constexpr int KROW = D / 8 + 1;      // padded K row, in chunks
+    static constexpr int VROW = D / 8 + 4;      // padded V row, in chunks
+    static constexpr int KSZ = HK * KROW;
+    static constexpr int STAGE = KSZ + HK * VROW;  // K then V, in 16-byte chunks
+    static constexpr int CPT = CH / NT;         // chunks per thread, per tensor
+    static_assert(CH % NT == 0, "unsupported step geometry");
 };
 
 template <int D, int BN>
@@ -188,66 +189,55 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         qf[ds] = __builtin_bit_cast(bf16x8, x);
     }
 
-    // per-thread load slots (fixed for the kernel): K chunk i is key row kr[i],
-    // 16-byte column kc[i]; V block j covers keys 4*vk[j]..+3, head-dim 8*vc..+7
-    int koff[G::KPT], kr[G::KPT], klds[G::KPT];
+    // per-thread load slots (fixed for the kernel): chunk i of a step is key
+    // row kr[i], 16-byte column kc[i], for K and V alike
+    int goff[G::CPT], kr[G::CPT], klds[G::CPT], vlds[G::CPT];
 #pragma unroll
-    for (int i = 0; i < G::KPT; ++i) {
+    for (int i = 0; i < G::CPT; ++i) {
         const int C = tid + i * NT, r = C / (D / 8), c = C % (D / 8);
         kr[i] = r;
-        koff[i] = r * rs * 2 + c * 16;
-        const int lr = kperm(r);
-        klds[i] = lr * (D / 8) + (c ^ swz(lr));
+        goff[i] = r * rs * 2 + c * 16;
+        klds[i] = kperm(r) * G::KROW + c;
+        vlds[i] = G::KSZ + r * G::VROW + c;
     }
-    const int vc = tid % (D / 8);              // V block: head-dim entries 8*vc..+7
-    const int vk = tid / (D / 8);              //          keys VK*vk..+VK-1 of the step
-    const int voff = vk * G::VK * rs * 2 + vc * 16;
 
-    u32x4 kreg[G::KPT];
-    u32x4 vreg[G::VK];
+    u32x4 kreg[G::CPT], vreg[G::CPT];
     auto load_step = [&](int key0) {
         const char *kb = Kb + (int64_t)key0 * rs * 2;
         const char *vb = Vb + (int64_t)key0 * rs * 2;
         if (key0 + HK <= N) {
 #pragma unroll
-            for (int i = 0; i < G::KPT; ++i)
-                kreg[i] = *(const u32x4 *)(kb + koff[i]);
-#pragma unroll
-            for (int r = 0; r < G::VK; ++r)
-                vreg[r] = *(const u32x4 *)(vb + voff + r * rs * 2);
+            for (int i = 0; i < G::CPT; ++i) {
+                kreg[i] = *(const u32x4 *)(kb + goff[i]);
+                vreg[i] = *(const u32x4 *)(vb + goff[i]);
+            }
         } else {
             const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int i = 0; i < G::KPT; ++i)
-                kreg[i] = (key0 + kr[i] < N) ? *(const u32x4 *)(kb + koff[i]) : z;
-#pragma unroll
-            for (int r = 0; r < G::VK; ++r)
-                vreg[r] = (key0 + G::VK * vk + r < N) ? *(const u32x4 *)(vb + voff + r * rs * 2) : z;
-        }
-    };
-    auto store_step = [&](int stage) {
-        u32x4 *Ks = smem + stage * G::STAGE;
-        char *Vs = (char *)(Ks + G::KCH);
-#pragma unroll
-        for (int i = 0; i < G::KPT; ++i)
-            Ks[klds[i]] = kreg[i];
-        // VK keys x 8 head-dim entries -> 8 rows of V^T holding VK keys (2*VK bytes) each
-        constexpr int PER_CHUNK = 8 / G::VK;    // key groups per 16-byte chunk
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            const int lr = vt_row(vc * 8 + e);
-            char *dst = Vs + (lr * (HK / 8) + ((vk / PER_CHUNK) ^ swz(lr))) * 16 + (vk % PER_CHUNK) * 2 * G::VK;
-            if constexpr (G::VK == 4) {
-                u32x2 o;
-                o[0] = __builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel);
-                o[1] = __builtin_amdgcn_perm(vreg[3][e >> 1], vreg[2][e >> 1], sel);
-                *(u32x2 *)dst = o;
-            } else {
-                *(uint32_t *)dst = __builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel);
+            for (int i = 0; i < G::CPT; ++i) {
+                const bool ok = key0 + kr[i] < N;
+                kreg[i] = ok ? *(const u32x4 *)(kb + goff[i]) : z;
+                vreg[i] = ok ? *(const u32x4 *)(vb + goff[i]) : z;
             }
         }
     };
+    auto store_step = [&](int stage) {
+        u32x4 *St = smem + stage * G::STAGE;
+#pragma unroll
+        for (int i = 0; i < G::CPT; ++i) {
+            St[klds[i]] = kreg[i];
+            St[vlds[i]] = vreg[i];
+        }
+    };
+
+    // This lane's slot as a source of the transposed V read: key row 8g + a of
+    // the 16-key group, 4 head-dim entries starting at sigma(16*(lane/16 % 2) + 4b),
+    // where lane % 16 = 4a + b.  The lane that receives column i of a 32-entry
+    // block then holds head-dim entry sigma(i) = 16*((i>>2)&1) + 4*(i>>3) + (i&3),
+    // which makes the O^T accumulator layout give every lane 16 consecutive
+    // head-dim entries (16*g + v, v = 0..15).
+    const int ts = lane & 15, tb = ts & 3;
+    const int vtr = ((8 * g + (ts >> 2)) * G::VROW) * 16 + (16 * (tb & 1) + 8 * ((lane >> 4) & 1) + 4 * (tb >> 1)) * 2;
 
     f32x16 O[D / 32];
 #pragma unroll
@@ -282,7 +272,7 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
             load_step(kt_n * BN + sub_n * HK);
 
         const u32x4 *Ks = smem + stage * G::STAGE;
-        const u32x4 *Vs = Ks + G::KCH;
+        const char *Vs = (const char *)(Ks + G::KSZ);
         if (sub == 0) {
             m_before = m_run;
             m_tile = -INFINITY;
@@ -296,10 +286,10 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     S[kb][v] = 0.f;
-                const int lr = kb * 32 + lq;
+                const u32x4 *ka = Ks + (kb * 32 + lq) * G::KROW + g;
 #pragma unroll
                 for (int ds = 0; ds < D / 16; ++ds) {
-                    const u32x4 a = Ks[lr * (D / 8) + ((2 * ds + g) ^ swz(lr))];
+                    const u32x4 a = ka[2 * ds];
                     S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ds], S[kb],
                                                                     0, 0, 0);
                 }
@@ -327,6 +317,9 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
             m_tile = fmaxf(m_tile, m_loc);
 
             // ---- online softmax ----
+            // Exponents are taken against the exact running max, so the largest
+            // weight of a row is exactly 1 (exact in bf16); O and l are rescaled
+            // only when some query's max moved (wave-uniform test).
             const float m_new = fmaxf(m_run, m_loc);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             const float neg = -m_new;
@@ -353,10 +346,12 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
             // ---- O^T += V^T P^T ----
 #pragma unroll
             for (int eb = 0; eb < D / 32; ++eb) {
-                const int lr = eb * 32 + lq;
 #pragma unroll
                 for (int ks = 0; ks < HK / 16; ++ks) {
-                    const u32x4 a = Vs[lr * (HK / 8) + ((2 * ks + g) ^ swz(lr))];
+                    const char *va = Vs + vtr + ks * 16 * G::VROW * 16 + eb * 64;
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va + 4 * G::VROW * 16));
+                    const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                     O[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), P[ks], O[eb],
                                                                     0, 0, 0);
                 }

@@ -18,7 +18,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblite_attn.so")
+LIB_PATH = os.environ.get("LITE_ATTN_LIBRARY") or os.path.join(_HERE, "liblite_attn.so")
 
 LITE_BF16, LITE_FP32 = 0, 1
 LITE_OK = 0

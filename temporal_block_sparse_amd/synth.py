@@ -115,11 +115,12 @@ class Trajectory:
 
 
 def random_qkv(batch, seqlen, heads, head_dim, dtype=torch.float32, seed=0, scale=1.0, device="cpu"):
-    """Plain N(0, scale^2) BSHD tensors (for shape sweeps and edge cases)."""
+    """Plain BSHD tensors for shape sweeps and edge cases: q, k ~ N(0, scale^2),
+    v ~ N(0, 1) (unit-variance values, as in the workload recipe)."""
     g = _gen(device, subseed(seed, "q", 0, 0))
     out = []
-    for _ in range(3):
-        out.append((scale * torch.randn(batch, seqlen, heads, head_dim, generator=g, device=device)).to(dtype))
+    for sc in (scale, scale, 1.0):
+        out.append((sc * torch.randn(batch, seqlen, heads, head_dim, generator=g, device=device)).to(dtype))
     return tuple(out)
 
 
