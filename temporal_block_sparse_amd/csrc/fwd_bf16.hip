@@ -21,25 +21,25 @@
 // * A k-tile is consumed in steps of 64 keys.  The online softmax is updated
 //   per step (exact in any grouping); the QK-Skip test uses the maximum over
 //   all steps of the tile against the running max taken before its first step.
-// * Two 64-key steps are double-buffered in LDS (64 KB at head_dim 128), so
-//   two workgroups fit on a CU and each SIMD interleaves two waves: one wave's
-//   softmax (VALU, v_exp) runs under the other's MFMAs.  The next step's
-//   global loads are issued before the current step's MFMAs and land in the
-//   other buffer afterwards; one barrier per step.
-// * K rows are stored in LDS with rows 4..7 and 8..11 of every 16 swapped, so
-//   that the 8 scores a lane holds per 16-key MFMA step are 8 consecutive
-//   keys; V is stored transposed (V^T, e-major) via an in-register 4x8
-//   transpose (v_perm_b32), so the PV A-operand is one 16-byte LDS read, with
-//   its rows permuted so a lane's O^T values are 16 consecutive head-dim
-//   entries (two 16-byte global stores).
-// * 16-byte LDS chunks are XOR-swizzled per row against bank conflicts.
-// * Loads use a wave-uniform tile base plus a per-lane 32-bit offset fixed for
-//   the whole kernel; only the ragged last tile takes the predicated path.
+// * K and V steps go global -> LDS by direct-to-LDS loads
+//   (global_load_lds_dwordx4): no staging registers, no LDS store
+//   instructions.  Two steps are double-buffered (64 KB at head_dim 128), so
+//   two workgroups fit on a CU and each SIMD interleaves two waves: one
+//   wave's softmax (VALU, v_exp) runs under the other's MFMAs.  The next
+//   step's loads are issued before the current step's MFMAs; one barrier per
+//   step.
+// * K rows sit in LDS with rows 4..7 and 8..11 of every 16 swapped, so the 8
+//   scores a lane holds per 16-key MFMA step are 8 consecutive keys.  V stays
+//   in natural (key x head-dim) layout and the PV A-operand (V^T) is read with
+//   ds_read_b64_tr_b16, the LDS transpose read.
+// * 16-byte chunks (K) and 64-byte segments (V) are XOR-swizzled per row,
+//   measured free of bank conflicts for these read patterns.
+// * Workgroups run in plain row order: at any time all XCDs work on the q-tiles
+//   of one or two heads, whose K/V (39 MB per head at 75,600 tokens) then stay
+//   in the 256 MB Infinity Cache, so L2 misses are served there, not by HBM.
 // * The QK-Skip vote is one ballot per wave and tile; a wave that wants to
 //   keep the tile sets its bit in an LDS keep-vector with one atomic OR.  The
 //   mask row is written once, in the epilogue.
-// * Workgroups are remapped so each XCD runs contiguous q-tiles of a head
-//   (shared K/V in that XCD's L2).
 #include "lite_attn_internal.h"
 
 #include <math.h>
@@ -53,6 +53,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 #define LDS_S16X4(p) ((__attribute__((address_space(3))) s16x4 *)(p))
+#define LDS_VOID(p) ((__attribute__((address_space(3))) void *)(p))
 
 constexpr int BM = 128;       // queries per workgroup (one q-tile)
 constexpr int NWAVES = 4;
@@ -129,26 +130,45 @@ struct LiveTiles {
     }
 };
 
-// LDS layout of one 64-key step.
-// K: row-major (key x head-dim) with the kperm row order, rows padded by one
-//    16-byte chunk; the 16-byte MFMA A-operand reads of 32 consecutive rows
-//    are then free of bank conflicts.
-// V: row-major (key x head-dim), natural row order, rows padded by 64 bytes.
-//    The PV A-operand (V^T: 8 consecutive keys of one head-dim entry per lane)
-//    is read with ds_read_b64_tr_b16: in each 16-lane group, lane 4a+b points
-//    at 4 head-dim entries of key row a, and the hardware hands lane i the
-//    entries of column i for the 4 rows.  The 64-byte pad puts those 4 rows
-//    in different banks.
+// LDS layout of one 64-key step.  K and V arrive by direct-to-LDS loads
+// (global_load_lds_dwordx4): each wave instruction writes 64 consecutive
+// 16-byte chunks, lane i to chunk i, so the layout is any permutation of the
+// step's chunks -- chosen per lane by the global address it loads.
+// K: key x head-dim with the kperm row order; chunk c of LDS row r holds
+//    head-dim chunk c ^ fk(r).  The MFMA A-operand reads (16-byte, 16 lanes
+//    per LDS cycle over 32 consecutive rows) then hit 16 distinct 16-byte bank
+//    groups: fk(r) = r mod 16 for 16-chunk rows, (r/2) mod 8 for 8-chunk rows.
+// V: key x head-dim, natural row order; its 64-byte segments are XOR-swizzled
+//    by the row so that the 4 rows touched by one ds_read_b64_tr_b16 (see the
+//    PV step) land in 4 different bank groups.
 template <int D>
 struct Geo {
-    static constexpr int CH = HK * D / 8;       // 16-byte chunks of a K (or V) step
-    static constexpr int KROW = D / 8 + 1;      // padded K row, in chunks
-    static constexpr int VROW = D / 8 + 4;      // padded V row, in chunks
-    static constexpr int KSZ = HK * KROW;
-    static constexpr int STAGE = KSZ + HK * VROW;  // K then V, in 16-byte chunks
-    static constexpr int CPT = CH / NT;         // chunks per thread, per tensor
-    static_assert(CH % NT == 0, "unsupported step geometry");
+    static constexpr int CPR = D / 8;            // 16-byte chunks per row
+    static constexpr int CH = HK * CPR;          // chunks of a K (or V) step
+    static constexpr int STAGE = 2 * CH;         // K then V, in chunks
+    static constexpr int IPW = CH / 64 / NWAVES; // DMA instructions per wave, per tensor
+    static_assert(CH % (64 * NWAVES) == 0, "unsupported step geometry");
 };
+
+// One 16-byte direct-to-LDS load: each lane's `src`, into `dst` + 16 * lane
+// (dst is wave-uniform).
+__device__ __forceinline__ void dma16(const char *src, char *dst)
+{
+    __builtin_amdgcn_global_load_lds((const void *)src, LDS_VOID(dst), 16, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ int k_swz(int r)
+{
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// chunk offset (within a row) that the 64-byte-segment swizzle of row r applies
+template <int D>
+__device__ __forceinline__ int v_swz(int r)
+{
+    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
 
 template <int D, int BN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
@@ -162,7 +182,7 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, lq = lane & 31;
     const int N = p.N, H = p.H, Tq = p.Tq, Tk = p.Tk, W = p.W;
-    const int64_t row = xcd_remap(blockIdx.x, p.rows);
+    const int64_t row = blockIdx.x;
     const int qt = (int)(row % Tq);
     const int64_t bh = row / Tq;
     const int h = (int)(bh % H), b = (int)(bh / H);
@@ -189,44 +209,42 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         qf[ds] = __builtin_bit_cast(bf16x8, x);
     }
 
-    // per-thread load slots (fixed for the kernel): chunk i of a step is key
-    // row kr[i], 16-byte column kc[i], for K and V alike
-    int goff[G::CPT], kr[G::CPT], klds[G::CPT], vlds[G::CPT];
+    // Direct-to-LDS slots (fixed for the kernel): DMA instruction i of this wave
+    // fills LDS chunks [(i*NWAVES + wave)*64, +64) of the K (and V) step; this
+    // lane's chunk comes from key row kr[i], head-dim chunk kc[i] (K) / vc[i] (V).
+    int kr[G::IPW], kgo[G::IPW], vr[G::IPW], vgo[G::IPW];
 #pragma unroll
-    for (int i = 0; i < G::CPT; ++i) {
-        const int C = tid + i * NT, r = C / (D / 8), c = C % (D / 8);
-        kr[i] = r;
-        goff[i] = r * rs * 2 + c * 16;
-        klds[i] = kperm(r) * G::KROW + c;
-        vlds[i] = G::KSZ + r * G::VROW + c;
+    for (int i = 0; i < G::IPW; ++i) {
+        const int P = (i * NWAVES + wave) * 64 + lane;
+        const int lr = P / G::CPR, pos = P % G::CPR;
+        kr[i] = kperm(lr);
+        kgo[i] = kr[i] * rs * 2 + (pos ^ k_swz<D>(lr)) * 16;
+        vr[i] = lr;
+        vgo[i] = lr * rs * 2 + (pos ^ v_swz<D>(lr)) * 16;
     }
-
-    u32x4 kreg[G::CPT], vreg[G::CPT];
-    auto load_step = [&](int key0) {
+    // Issue the DMA of one 64-key step into LDS stage `stage`.  Keys past the
+    // end of the sequence are clamped to the last key: their logits are set
+    // to -inf before use, so their K and V rows never contribute.
+    auto load_step = [&](int key0, int stage) {
+        char *kdst = (char *)(smem + stage * G::STAGE) + wave * 64 * 16;
+        char *vdst = kdst + G::CH * 16;
         const char *kb = Kb + (int64_t)key0 * rs * 2;
         const char *vb = Vb + (int64_t)key0 * rs * 2;
         if (key0 + HK <= N) {
 #pragma unroll
-            for (int i = 0; i < G::CPT; ++i) {
-                kreg[i] = *(const u32x4 *)(kb + goff[i]);
-                vreg[i] = *(const u32x4 *)(vb + goff[i]);
+            for (int i = 0; i < G::IPW; ++i) {
+                dma16(kb + kgo[i], kdst + i * NWAVES * 64 * 16);
+                dma16(vb + vgo[i], vdst + i * NWAVES * 64 * 16);
             }
         } else {
-            const u32x4 z = {0u, 0u, 0u, 0u};
+            const int64_t back = (int64_t)rs * 2;
 #pragma unroll
-            for (int i = 0; i < G::CPT; ++i) {
-                const bool ok = key0 + kr[i] < N;
-                kreg[i] = ok ? *(const u32x4 *)(kb + goff[i]) : z;
-                vreg[i] = ok ? *(const u32x4 *)(vb + goff[i]) : z;
+            for (int i = 0; i < G::IPW; ++i) {
+                const int ko = key0 + kr[i] < N ? kgo[i] : kgo[i] - (int)((key0 + kr[i] - (N - 1)) * back);
+                const int vo = key0 + vr[i] < N ? vgo[i] : vgo[i] - (int)((key0 + vr[i] - (N - 1)) * back);
+                dma16(kb + ko, kdst + i * NWAVES * 64 * 16);
+                dma16(vb + vo, vdst + i * NWAVES * 64 * 16);
             }
-        }
-    };
-    auto store_step = [&](int stage) {
-        u32x4 *St = smem + stage * G::STAGE;
-#pragma unroll
-        for (int i = 0; i < G::CPT; ++i) {
-            St[klds[i]] = kreg[i];
-            St[vlds[i]] = vreg[i];
         }
     };
 
@@ -236,8 +254,12 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     // block then holds head-dim entry sigma(i) = 16*((i>>2)&1) + 4*(i>>3) + (i&3),
     // which makes the O^T accumulator layout give every lane 16 consecutive
     // head-dim entries (16*g + v, v = 0..15).
+    // Rows 8g + a + 16ks + 4h keep (row & 3) = a and ((row >> 1) & 1) = a >> 1,
+    // so the segment swizzle of the row depends only on this lane's a.
     const int ts = lane & 15, tb = ts & 3;
-    const int vtr = ((8 * g + (ts >> 2)) * G::VROW) * 16 + (16 * (tb & 1) + 8 * ((lane >> 4) & 1) + 4 * (tb >> 1)) * 2;
+    const int vtr_row = 8 * g + (ts >> 2);
+    const int vtr_col = (16 * (tb & 1) + 8 * ((lane >> 4) & 1) + 4 * (tb >> 1)) * 2;  // bytes in a 64-B segment
+    const int vtr_seg = v_swz<D>(vtr_row) / 4;                                       // segment XOR
 
     f32x16 O[D / 32];
 #pragma unroll
@@ -252,10 +274,8 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     it.init(mrow, p.skiplist ? p.skiplist + row * (1 + Tk) : nullptr, Tk);
     int kt = it.next();
     int sub = 0;
-    if (kt >= 0) {
-        load_step(kt * BN);
-        store_step(0);
-    }
+    if (kt >= 0)
+        load_step(kt * BN, 0);
     __syncthreads();
     int kt_after = kt >= 0 ? it.next() : -1;  // next live tile after kt
     int stage = 0;
@@ -269,10 +289,10 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         }
         const int key0 = kt * BN + sub * HK;
         if (kt_n >= 0 && kt_n * BN + sub_n * HK < N)
-            load_step(kt_n * BN + sub_n * HK);
+            load_step(kt_n * BN + sub_n * HK, stage ^ 1);
 
         const u32x4 *Ks = smem + stage * G::STAGE;
-        const char *Vs = (const char *)(Ks + G::KSZ);
+        const char *Vs = (const char *)(Ks + G::CH);
         if (sub == 0) {
             m_before = m_run;
             m_tile = -INFINITY;
@@ -286,10 +306,12 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     S[kb][v] = 0.f;
-                const u32x4 *ka = Ks + (kb * 32 + lq) * G::KROW + g;
+                const int kr0 = kb * 32 + lq;
+                const u32x4 *ka = Ks + kr0 * G::CPR;
+                const int ksw = k_swz<D>(kr0);
 #pragma unroll
                 for (int ds = 0; ds < D / 16; ++ds) {
-                    const u32x4 a = ka[2 * ds];
+                    const u32x4 a = ka[(2 * ds + g) ^ ksw];
                     S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ds], S[kb],
                                                                     0, 0, 0);
                 }
@@ -348,9 +370,9 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
             for (int eb = 0; eb < D / 32; ++eb) {
 #pragma unroll
                 for (int ks = 0; ks < HK / 16; ++ks) {
-                    const char *va = Vs + vtr + ks * 16 * G::VROW * 16 + eb * 64;
+                    const char *va = Vs + (vtr_row + 16 * ks) * G::CPR * 16 + ((eb ^ vtr_seg) * 64) + vtr_col;
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va));
-                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va + 4 * G::VROW * 16));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va + 4 * G::CPR * 16));
                     const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                     O[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), P[ks], O[eb],
                                                                     0, 0, 0);
@@ -365,8 +387,6 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
                 atomicOr(&keep[kt >> 5], 1u << (kt & 31));
         }
 
-        if (kt_n >= 0 && kt_n * BN + sub_n * HK < N)
-            store_step(stage ^ 1);
         __syncthreads();
         if (sub_n == 0) {
             kt = kt_after;

@@ -30,7 +30,7 @@ fwd_fp32_kernel(FwdParams p)
 
     const int lane = threadIdx.x;
     const int N = p.N, H = p.H, Tq = p.Tq, Tk = p.Tk, W = p.W;
-    const int64_t row = xcd_remap(blockIdx.x, p.rows);
+    const int64_t row = blockIdx.x;
     const int qt = (int)(row % Tq);
     const int64_t bh = row / Tq;
     const int h = (int)(bh % H), b = (int)(bh / H);

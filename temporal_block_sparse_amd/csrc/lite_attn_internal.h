@@ -28,15 +28,4 @@ hipError_t launch_build_skiplist(const uint32_t *mask, int32_t *skiplist, int64_
                                  hipStream_t stream);
 hipError_t launch_reset_mask(uint32_t *mask, int64_t words, hipStream_t stream);
 
-// Row id -> XCD-aware dispatch order.  Workgroups are handed to the 8 XCDs
-// round-robin (workgroup i runs on XCD i % 8).  Remapping gives each XCD one
-// contiguous range of rows, so the q-tiles of one head that run at the same
-// time share the XCD's L2 while they stream the same K/V tiles.
-__device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t n)
-{
-    const int64_t q = n >> 3, r = n & 7;
-    const int64_t x = i & 7, j = i >> 3;
-    return x * q + (x < r ? x : r) + j;
-}
-
 }  // namespace lite_attn
