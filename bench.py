@@ -335,7 +335,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "traffic_note": traffic_note,
-                     "kernel": "fwd_bf16_kernel<128,128>", "kernel_source_sha256_16": src_hash},
+                     "kernel": "fwd_bf16_kernel<%d, %d, %s>" % (wl.head_dim, wl.tile_n,
+                                                                 "true" if args.path == "skiplist" else "false"),
+                     "kernel_source_sha256_16": src_hash},
         "cpu_baseline": cpu,
         "tau_sweep": sweep,
     }

@@ -1,7 +1,5 @@
 // Skip-masked tiled attention forward, bf16 in / bf16 out, fp32 accumulation,
-// hand-written for gfx950 (CDNA4): one workgroup of 4 wave64s per
-// (batch, head, q-tile of 128 queries); each wave owns 32 queries; two
-// workgroups share a CU.
+// hand-written for gfx950 (CDNA4).
 //
 // Method (LiteAttention README, "QK-Skip Algorithm" and "Full-Stage
 // Elimination"; arXiv 2511.11062 abstract): k-tiles set in the Skip-Mask are
@@ -12,37 +10,60 @@
 // the tile, below the threshold for every query of the q-tile) and, when it
 // passes, is marked in the mask carried to the next denoising step.
 //
+// Work decomposition
+// * One workgroup of 8 wave64s serves two adjacent q-tiles (128 queries each)
+//   of one (batch, head): waves 0-3 the even q-tile "A", waves 4-7 the odd
+//   q-tile "B"; each wave owns 32 queries.  Wave w and wave w + 4 share a SIMD.
+// * The workgroup walks the union of A's and B's live k-tiles in descending
+//   order, in steps of 64 keys.  A wave computes only the steps its own q-tile
+//   visits, so each q-tile sees exactly its own live tiles in its own order:
+//   decisions and outputs are those of a one-q-tile kernel.  Both q-tiles
+//   read the same K/V from LDS, so one copy of a step serves 256 queries.
+// * Ping-pong: every step is two barrier-separated phases.  In the first,
+//   A's waves run their MFMAs (PV of the previous step, then QK^T of this one)
+//   while B's waves run the softmax of the previous step; in the second the
+//   roles swap.  On every SIMD one wave feeds the matrix core while the other
+//   runs its exponentials on the vector ALU, instead of both waves competing
+//   for one unit.  The MFMA phases are software-pipelined by hand: the LDS
+//   reads run four MFMAs ahead of their use.
+//
 // gfx950 layout choices
 // * Both contractions are transposed, S^T = K Q^T and O^T = V^T P^T, on
 //   v_mfma_f32_32x32x16_bf16.  The accumulator layout then gives every lane a
 //   single query (lane % 32): its row max needs only in-register max plus one
 //   v_permlane32_swap with the other half-wave, P^T feeds the second MFMA
 //   straight from registers, and the O rescale uses the lane's own factor.
-// * A k-tile is consumed in steps of 64 keys.  The online softmax is updated
-//   per step (exact in any grouping); the QK-Skip test uses the maximum over
-//   all steps of the tile against the running max taken before its first step.
+// * The online softmax is updated per 64-key step (exact in any grouping);
+//   the QK-Skip test uses the maximum over all steps of the tile against the
+//   running max taken before its first step.
 // * K and V steps go global -> LDS by direct-to-LDS loads
 //   (global_load_lds_dwordx4): no staging registers, no LDS store
-//   instructions.  Two steps are double-buffered (64 KB at head_dim 128), so
-//   two workgroups fit on a CU and each SIMD interleaves two waves: one
-//   wave's softmax (VALU, v_exp) runs under the other's MFMAs.  The next
-//   step's loads are issued before the current step's MFMAs; one barrier per
-//   step.
+//   instructions.  Three LDS stages (96 KB at head_dim 128): step u's K is
+//   read in the two phases of step u, its V in the two phases of step u + 1,
+//   and step u + 1 is loaded meanwhile.  A's waves issue the loads during
+//   their QK^T MFMAs, after their PV reads, so no LDS read of this kernel ever
+//   waits for a load in flight; the loads complete at the end of the step.
 // * K rows sit in LDS with rows 4..7 and 8..11 of every 16 swapped, so the 8
 //   scores a lane holds per 16-key MFMA step are 8 consecutive keys.  V stays
 //   in natural (key x head-dim) layout and the PV A-operand (V^T) is read with
 //   ds_read_b64_tr_b16, the LDS transpose read.
 // * 16-byte chunks (K) and 64-byte segments (V) are XOR-swizzled per row,
 //   measured free of bank conflicts for these read patterns.
-// * Workgroups run in plain row order: at any time all XCDs work on the q-tiles
-//   of one or two heads, whose K/V (39 MB per head at 75,600 tokens) then stay
-//   in the 256 MB Infinity Cache, so L2 misses are served there, not by HBM.
+// * The live tiles are iterated from registers: the mask words of a row are
+//   held one per lane (two words per lane for up to 128 words), a Skip-List
+//   64 entries at a time, so finding the next tile costs scalar instructions,
+//   not a memory round trip per tile.
+// * Workgroups run in plain order: at any time all XCDs work on the q-tiles of
+//   one or two heads, whose K/V (39 MB per head at 75,600 tokens) then stay in
+//   the 256 MB Infinity Cache, so L2 misses are served there, not by HBM.
 // * The QK-Skip vote is one ballot per wave and tile; a wave that wants to
-//   keep the tile sets its bit in an LDS keep-vector with one atomic OR.  The
-//   mask row is written once, in the epilogue.
+//   keep the tile sets its bit in its q-tile's LDS keep-vector with one atomic
+//   OR.  Each mask row is written once, in the epilogue.
 #include "lite_attn_internal.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace lite_attn {
 namespace {
@@ -55,11 +76,15 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 #define LDS_S16X4(p) ((__attribute__((address_space(3))) s16x4 *)(p))
 #define LDS_VOID(p) ((__attribute__((address_space(3))) void *)(p))
 
-constexpr int BM = 128;       // queries per workgroup (one q-tile)
-constexpr int NWAVES = 4;
+constexpr int BM = 128;       // queries per q-tile
+constexpr int NWAVES = 8;     // 4 per q-tile, 2 q-tiles per workgroup
 constexpr int NT = 64 * NWAVES;
 constexpr int HK = 64;        // keys per step
 constexpr int MAXW = 128;     // mask words per row (Tk <= 4096)
+constexpr int AHEAD = 4;      // MFMAs by which the LDS reads run ahead
+
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int SG_MFMA = 0x008, SG_VMEM = 0x010, SG_DS_READ = 0x100;
 
 // LDS row r of a K step holds key kperm(r): rows 4..7 and 8..11 of each 16 swapped.
 __device__ __forceinline__ int kperm(int r)
@@ -78,57 +103,147 @@ __device__ __forceinline__ float other_half(float x)
     return (threadIdx.x & 32) ? a : b;
 }
 
-// Live k-tiles of one row in visiting order (descending), from the Skip-List
-// when one is given, else from the mask words.  All values are wave-uniform.
-struct LiveTiles {
-    const uint32_t *mask;
-    const int32_t *list;
-    int Tk, W, w, idx, cnt;
-    uint32_t cur;
+// LDS atomic OR whose completion is awaited in the same asm block.  Written
+// out so that the compiler does not make it wait for the direct-to-LDS loads
+// in flight, which never touch the keep-vector.
+__device__ __forceinline__ void lds_or(uint32_t *p, uint32_t bits)
+{
+    const uint32_t a = (uint32_t)(size_t)LDS_VOID(p);
+    asm volatile("ds_or_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(bits) : "memory");
+}
 
-    __device__ uint32_t live_word(int wi) const
+// Live k-tiles of one row in visiting order (descending), from the Skip-List
+// (LIST) or from the mask words; `none` for a q-tile that does not exist.
+// Returned values are wave-uniform.
+template <bool LIST>
+struct LiveTiles {
+    uint32_t wlo, whi;     // live bits of mask words `lane` and `lane + 64`
+    uint64_t nzlo, nzhi;   // which words have a live bit
+    int w;                 // word `cur` came from
+    uint32_t cur;          // its live bits not yet returned
+    const int32_t *list;
+    int32_t chunk;         // list entries [idx & ~63, +64), one per lane
+    int cnt, idx;
+    bool none;
+
+    __device__ __forceinline__ void init(const uint32_t *m, const int32_t *l, int tk, bool exists)
     {
-        uint32_t bits = mask ? ~mask[wi] : 0xffffffffu;
-        if (wi == W - 1 && (Tk & 31))
-            bits &= (1u << (Tk & 31)) - 1u;
-        return bits;
-    }
-    __device__ void init(const uint32_t *m, const int32_t *l, int tk)
-    {
-        mask = m;
+        const int lane = threadIdx.x & 63;
+        none = !exists;
         list = l;
-        Tk = tk;
-        W = (tk + 31) >> 5;
         idx = 0;
-        if (list) {
-            const int c = list[0];
+        cnt = 0;
+        w = 0;
+        cur = 0;
+        chunk = -1;
+        wlo = whi = 0;
+        nzlo = nzhi = 0;
+        if (none)
+            return;
+        if (LIST) {
+            const int c = __builtin_amdgcn_readfirstlane(l[0]);
             cnt = c < 0 ? 0 : (c > tk ? tk : c);
-            w = 0;
-            cur = 0;
+            chunk = lane < cnt ? l[1 + lane] : -1;
         } else {
-            cnt = 0;
-            w = W - 1;
-            cur = live_word(w);
+            const int W = (tk + 31) >> 5;
+            auto live = [&](int wi) -> uint32_t {
+                if (wi >= W)
+                    return 0u;
+                uint32_t bits = m ? ~m[wi] : 0xffffffffu;
+                if (wi == W - 1 && (tk & 31))
+                    bits &= (1u << (tk & 31)) - 1u;
+                return bits;
+            };
+            wlo = live(lane);
+            whi = live(lane + 64);
+            nzlo = __ballot(wlo != 0u);
+            nzhi = __ballot(whi != 0u);
+            w = W;
         }
     }
-    __device__ int next()
+    __device__ __forceinline__ int next(int tk)
     {
-        if (list) {
+        if (none)
+            return -1;
+        if (LIST) {
             if (idx >= cnt)
                 return -1;
-            const int kt = list[1 + idx++];
-            return (kt >= 0 && kt < Tk) ? kt : -1;
+            if (idx > 0 && (idx & 63) == 0) {
+                const int lane = threadIdx.x & 63;
+                chunk = idx + lane < cnt ? list[1 + idx + lane] : -1;
+            }
+            const int kt = __builtin_amdgcn_readlane(chunk, idx & 63);
+            ++idx;
+            return (kt >= 0 && kt < tk) ? kt : -1;
         }
-        while (cur == 0) {
-            if (w <= 0)
+        while (cur == 0u) {
+            // the highest word below w with a live bit
+            int nw = -1;
+            if (w > 64) {
+                const uint64_t mm = nzhi & (w - 64 >= 64 ? ~0ull : ((1ull << (w - 64)) - 1ull));
+                if (mm)
+                    nw = 127 - __builtin_clzll(mm);
+            }
+            if (nw < 0) {
+                const uint64_t mm = nzlo & (w >= 64 ? ~0ull : ((1ull << w) - 1ull));
+                if (mm)
+                    nw = 63 - __builtin_clzll(mm);
+            }
+            if (nw < 0) {
+                none = true;
                 return -1;
-            cur = live_word(--w);
+            }
+            w = nw;
+            cur = (uint32_t)__builtin_amdgcn_readlane((int)(nw < 64 ? wlo : whi), nw & 63);
         }
         const int bit = 31 - __builtin_clz(cur);
         cur &= ~(1u << bit);
         return w * 32 + bit;
     }
 };
+
+// The union of two rows' live tiles, descending; flags bit 0 / bit 1 say
+// whether q-tile A / B visits the returned tile.
+template <bool LIST>
+struct LivePair {
+    LiveTiles<LIST> a, b;
+    int na, nb;
+    __device__ __forceinline__ void init(const uint32_t *ma, const int32_t *la, const uint32_t *mb,
+                                         const int32_t *lb, int tk, bool has_b)
+    {
+        a.init(ma, la, tk, true);
+        b.init(mb, lb, tk, has_b);
+        na = a.next(tk);
+        nb = b.next(tk);
+    }
+    __device__ __forceinline__ int next(int &flags, int tk)
+    {
+        const int kt = na > nb ? na : nb;
+        if (kt < 0)
+            return -1;
+        flags = (na == kt ? 1 : 0) | (nb == kt ? 2 : 0);
+        if (na == kt)
+            na = a.next(tk);
+        if (nb == kt)
+            nb = b.next(tk);
+        return kt;
+    }
+};
+
+// One 64-key step of the union walk (wave-uniform).
+struct Step {
+    int kt;    // k-tile, -1 = none
+    int sub;   // 64-key step within the tile
+    int fl;    // bit 0: q-tile A visits the tile, bit 1: q-tile B
+    int key0;  // first key
+};
+
+// One 16-byte direct-to-LDS load: each lane's `src`, into `dst` + 16 * lane
+// (dst is wave-uniform).
+__device__ __forceinline__ void dma16(const char *src, char *dst)
+{
+    __builtin_amdgcn_global_load_lds((const void *)src, LDS_VOID(dst), 16, 0, 0);
+}
 
 // LDS layout of one 64-key step.  K and V arrive by direct-to-LDS loads
 // (global_load_lds_dwordx4): each wave instruction writes 64 consecutive
@@ -143,19 +258,12 @@ struct LiveTiles {
 //    PV step) land in 4 different bank groups.
 template <int D>
 struct Geo {
-    static constexpr int CPR = D / 8;            // 16-byte chunks per row
-    static constexpr int CH = HK * CPR;          // chunks of a K (or V) step
-    static constexpr int STAGE = 2 * CH;         // K then V, in chunks
-    static constexpr int IPW = CH / 64 / NWAVES; // DMA instructions per wave, per tensor
-    static_assert(CH % (64 * NWAVES) == 0, "unsupported step geometry");
+    static constexpr int CPR = D / 8;       // 16-byte chunks per row
+    static constexpr int CH = HK * CPR;     // chunks of a K (or V) step
+    static constexpr int STAGE = 2 * CH;    // K then V, in chunks
+    static constexpr int IPA = CH / 64 / 4; // DMA instructions per A-wave, per tensor
+    static_assert(CH % (64 * 4) == 0, "unsupported step geometry");
 };
-
-// One 16-byte direct-to-LDS load: each lane's `src`, into `dst` + 16 * lane
-// (dst is wave-uniform).
-__device__ __forceinline__ void dma16(const char *src, char *dst)
-{
-    __builtin_amdgcn_global_load_lds((const void *)src, LDS_VOID(dst), 16, 0, 0);
-}
 
 template <int D>
 __device__ __forceinline__ int k_swz(int r)
@@ -170,36 +278,46 @@ __device__ __forceinline__ int v_swz(int r)
     return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-template <int D, int BN>
+template <int D, int BN, bool LIST>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(FwdParams p, float c2, float tau2)
 {
     using G = Geo<D>;
     constexpr int SPT = BN / HK;  // steps per k-tile
-    __shared__ u32x4 smem[2 * G::STAGE];
-    __shared__ uint32_t keep[MAXW];
+    // Three distinct LDS objects, one per pipeline stage: the compiler can then
+    // tell a stage being read from the stage being filled by DMA.
+    __shared__ u32x4 stage0[G::STAGE];
+    __shared__ u32x4 stage1[G::STAGE];
+    __shared__ u32x4 stage2[G::STAGE];
+    __shared__ uint32_t keep[2][MAXW];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+    const int half = wave >> 2;                                 // 0: q-tile A, 1: q-tile B
+    const int wq = wave & 3;                                    // 32-query block in the q-tile
     const int g = lane >> 5, lq = lane & 31;
     const int N = p.N, H = p.H, Tq = p.Tq, Tk = p.Tk, W = p.W;
-    const int64_t row = blockIdx.x;
-    const int qt = (int)(row % Tq);
-    const int64_t bh = row / Tq;
+    const int Tq2 = (Tq + 1) >> 1;
+    const int pq = (int)(blockIdx.x % Tq2);
+    const int64_t bh = blockIdx.x / Tq2;
     const int h = (int)(bh % H), b = (int)(bh / H);
-    const int rs = H * D;  // token stride (elements)
+    const bool has_b = 2 * pq + 1 < Tq;
+    const int64_t row_a = bh * Tq + 2 * pq;  // q-tile B is row_a + 1
+    const int qt = 2 * pq + half;            // this wave's q-tile
+    const int rs = H * D;                    // token stride (elements)
+    const int rs2 = rs * 2;                  // token stride (bytes)
     const int64_t base = (int64_t)b * N * rs + (int64_t)h * D;
     const __bf16 *Qb = (const __bf16 *)p.q + base;
     const char *Kb = (const char *)((const __bf16 *)p.k + base);
     const char *Vb = (const char *)((const __bf16 *)p.v + base);
-    const uint32_t *mrow = p.mask_in ? p.mask_in + row * W : nullptr;
     const bool vote = p.mask_out != nullptr;
 
-    if (tid < W)
-        keep[tid] = 0u;
+    if (tid < 2 * W)
+        keep[tid / W][tid % W] = 0u;
 
     // this lane's query and its Q^T B-operand fragments
-    const int qi = qt * BM + wave * 32 + lq;
-    const bool qvalid = qi < N;
+    const int qi = qt * BM + wq * 32 + lq;
+    const bool qvalid = qt < Tq && qi < N;
     bf16x8 qf[D / 16];
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
@@ -209,43 +327,43 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         qf[ds] = __builtin_bit_cast(bf16x8, x);
     }
 
-    // Direct-to-LDS slots (fixed for the kernel): DMA instruction i of this wave
-    // fills LDS chunks [(i*NWAVES + wave)*64, +64) of the K (and V) step; this
-    // lane's chunk comes from key row kr[i], head-dim chunk kc[i] (K) / vc[i] (V).
-    int kr[G::IPW], kgo[G::IPW], vr[G::IPW], vgo[G::IPW];
+    // Direct-to-LDS slots of the A-waves, which load every step (fixed for the
+    // kernel): DMA instruction i of A-wave wq fills LDS chunks
+    // [(i*4 + wq)*64, +64) of the K (and V) step; this lane's chunk comes from
+    // key row kr[i] (K) / vr[i] (V) of the step, at byte offset kgo[i] / vgo[i]
+    // from the step's first key.
+    int kr[G::IPA], kgo[G::IPA], vr[G::IPA], vgo[G::IPA];
 #pragma unroll
-    for (int i = 0; i < G::IPW; ++i) {
-        const int P = (i * NWAVES + wave) * 64 + lane;
+    for (int i = 0; i < G::IPA; ++i) {
+        const int P = (i * 4 + wq) * 64 + lane;
         const int lr = P / G::CPR, pos = P % G::CPR;
         kr[i] = kperm(lr);
-        kgo[i] = kr[i] * rs * 2 + (pos ^ k_swz<D>(lr)) * 16;
+        kgo[i] = kr[i] * rs2 + (pos ^ k_swz<D>(lr)) * 16;
         vr[i] = lr;
-        vgo[i] = lr * rs * 2 + (pos ^ v_swz<D>(lr)) * 16;
+        vgo[i] = lr * rs2 + (pos ^ v_swz<D>(lr)) * 16;
     }
-    // Issue the DMA of one 64-key step into LDS stage `stage`.  Keys past the
-    // end of the sequence are clamped to the last key: their logits are set
-    // to -inf before use, so their K and V rows never contribute.
-    auto load_step = [&](int key0, int stage) {
-        char *kdst = (char *)(smem + stage * G::STAGE) + wave * 64 * 16;
-        char *vdst = kdst + G::CH * 16;
-        const char *kb = Kb + (int64_t)key0 * rs * 2;
-        const char *vb = Vb + (int64_t)key0 * rs * 2;
-        if (key0 + HK <= N) {
-#pragma unroll
-            for (int i = 0; i < G::IPW; ++i) {
-                dma16(kb + kgo[i], kdst + i * NWAVES * 64 * 16);
-                dma16(vb + vgo[i], vdst + i * NWAVES * 64 * 16);
-            }
-        } else {
-            const int64_t back = (int64_t)rs * 2;
-#pragma unroll
-            for (int i = 0; i < G::IPW; ++i) {
-                const int ko = key0 + kr[i] < N ? kgo[i] : kgo[i] - (int)((key0 + kr[i] - (N - 1)) * back);
-                const int vo = key0 + vr[i] < N ? vgo[i] : vgo[i] - (int)((key0 + vr[i] - (N - 1)) * back);
-                dma16(kb + ko, kdst + i * NWAVES * 64 * 16);
-                dma16(vb + vo, vdst + i * NWAVES * 64 * 16);
-            }
-        }
+    // The loads of one step into one LDS stage.  Rows past the end of the
+    // sequence are clamped to key N-1 (their logits are set to -inf before
+    // use), so every address is in bounds.
+    struct DmaPlan {
+        const char *kb, *vb;
+        char *kdst, *vdst;
+        int over;  // first key - (N - 1): row r is clamped when r + over > 0
+    };
+    auto plan_step = [&](const Step &s, u32x4 *dst) __attribute__((always_inline)) {
+        DmaPlan d;
+        d.kdst = (char *)dst + wq * 64 * 16;
+        d.vdst = d.kdst + G::CH * 16;
+        d.kb = Kb + (int64_t)s.key0 * rs2;
+        d.vb = Vb + (int64_t)s.key0 * rs2;
+        d.over = s.key0 - (N - 1);
+        return d;
+    };
+    auto issue_dma = [&](const DmaPlan &d, int i) __attribute__((always_inline)) {
+        const int ko = kgo[i] - max(kr[i] + d.over, 0) * rs2;
+        const int vo = vgo[i] - max(vr[i] + d.over, 0) * rs2;
+        dma16(d.kb + ko, d.kdst + i * 4 * 64 * 16);
+        dma16(d.vb + vo, d.vdst + i * 4 * 64 * 16);
     };
 
     // This lane's slot as a source of the transposed V read: key row 8g + a of
@@ -269,65 +387,133 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
             O[eb][v] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
     float m_before = -INFINITY, m_tile = -INFINITY;
+    f32x16 S[HK / 32];       // raw logits of the step between QK^T and softmax
+    bf16x8 P[HK / 16];       // weights of the step between softmax and PV
+#pragma unroll
+    for (int kb = 0; kb < HK / 32; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            S[kb][v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < HK / 16; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            P[ks][j] = (__bf16)0.f;
 
-    LiveTiles it;
-    it.init(mrow, p.skiplist ? p.skiplist + row * (1 + Tk) : nullptr, Tk);
-    int kt = it.next();
-    int sub = 0;
-    if (kt >= 0)
-        load_step(kt * BN, 0);
-    __syncthreads();
-    int kt_after = kt >= 0 ? it.next() : -1;  // next live tile after kt
-    int stage = 0;
-
-    while (kt >= 0) {
-        // the step after this one
-        int kt_n = kt, sub_n = sub + 1;
-        if (sub_n == SPT) {
-            kt_n = kt_after;
-            sub_n = 0;
+    const uint32_t *mrow_a = p.mask_in ? p.mask_in + row_a * W : nullptr;
+    const uint32_t *mrow_b = (p.mask_in && has_b) ? p.mask_in + (row_a + 1) * W : nullptr;
+    const int32_t *list_a = LIST ? p.skiplist + row_a * (1 + Tk) : nullptr;
+    const int32_t *list_b = (LIST && has_b) ? p.skiplist + (row_a + 1) * (1 + Tk) : nullptr;
+    LivePair<LIST> it;
+    it.init(mrow_a, list_a, mrow_b, list_b, Tk, has_b);
+    int g_fl = 0;
+    int g_kt = it.next(g_fl, Tk);
+    int g_sub = 0;
+    auto gen = [&]() __attribute__((always_inline)) {
+        Step s;
+        s.kt = g_kt;
+        s.sub = g_sub;
+        s.fl = g_fl;
+        s.key0 = g_kt * BN + g_sub * HK;
+        if (g_kt >= 0 && ++g_sub == SPT) {
+            g_sub = 0;
+            g_kt = it.next(g_fl, Tk);
         }
-        const int key0 = kt * BN + sub * HK;
-        if (kt_n >= 0 && kt_n * BN + sub_n * HK < N)
-            load_step(kt_n * BN + sub_n * HK, stage ^ 1);
+        return s;
+    };
+    auto mine = [&](const Step &s) __attribute__((always_inline)) { return s.kt >= 0 && ((s.fl >> half) & 1); };
+    auto act = [&](const Step &s) __attribute__((always_inline)) { return mine(s) && s.key0 < N; };
+    auto loadable = [&](const Step &s) __attribute__((always_inline)) { return s.kt >= 0 && s.key0 < N; };
 
-        const u32x4 *Ks = smem + stage * G::STAGE;
-        const char *Vs = (const char *)(Ks + G::CH);
-        if (sub == 0) {
+    // ---- O^T += V^T P^T over one step (V in LDS stage vst) ----
+    // MFMA order ks-major over the D/32 independent accumulators; two
+    // transposed reads per MFMA, issued AHEAD MFMAs before their use.
+    auto pv_gemm = [&](const u32x4 *vst) __attribute__((always_inline)) {
+        constexpr int NEB = D / 32, NM = NEB * (HK / 16);
+        // lane offsets recomputed here, not kept live across the loop
+        int vl = vtr_row * G::CPR * 16 + vtr_col, vsg = vtr_seg;
+        asm volatile("" : "+v"(vl), "+v"(vsg));
+        const char *Vs = (const char *)(vst + G::CH) + vl;
+#pragma unroll
+        for (int ks = 0; ks < HK / 16; ++ks) {
+#pragma unroll
+            for (int eb = 0; eb < NEB; ++eb) {
+                const char *va = Vs + 16 * ks * G::CPR * 16 + ((eb ^ vsg) * 64);
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va + 4 * G::CPR * 16));
+                const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                O[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), P[ks], O[eb], 0, 0,
+                                                                0);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * AHEAD, 0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            if (m + AHEAD < NM)
+                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+        }
+    };
+
+    // ---- S^T = K Q^T over one step (K in LDS stage kst), raw logits ----
+    // MFMA order ds-major over the two 32-key blocks; one K read per MFMA,
+    // issued AHEAD MFMAs before its use.  With WD the loads of the next step
+    // (`dma`) go out one per two MFMAs.
+    auto s_gemm = [&](const u32x4 *kst, const DmaPlan &dma, auto with_dma) __attribute__((always_inline)) {
+        constexpr bool WD = decltype(with_dma)::value;
+        constexpr int NDS = D / 16, NM = (HK / 32) * NDS;
+        static_assert(NM == 4 * G::IPA, "one load pair per four MFMAs");
+        // Row kb*32 + lq, chunk (2*ds + g) ^ k_swz(row) = 2*ds ^ kc: the swizzle
+        // depends on the row only through lq.  Lane offsets recomputed here.
+        int kl = lq * G::CPR, kc = g ^ k_swz<D>(lq);
+        asm volatile("" : "+v"(kl), "+v"(kc));
+#pragma unroll
+        for (int kb = 0; kb < HK / 32; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                S[kb][v] = 0.f;
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+#pragma unroll
+            for (int kb = 0; kb < HK / 32; ++kb) {
+                const u32x4 a = kst[kb * 32 * G::CPR + kl + ((2 * ds) ^ kc)];
+                S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ds], S[kb], 0, 0,
+                                                                0);
+                // one (K, V) pair per four MFMAs: NM = 4 * IPA for both head dims
+                const int m = ds * (HK / 32) + kb;
+                if (WD && (m & 3) == 3)
+                    issue_dma(dma, m >> 2);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, AHEAD, 0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            if (m + AHEAD < NM)
+                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+            if (WD && (m & 1))
+                __builtin_amdgcn_sched_group_barrier(SG_VMEM, 1, 0);
+        }
+    };
+
+    // VALU phase of this wave's q-tile: online softmax of step s (logits in S),
+    // weights into P, then the QK-Skip vote once the whole tile has been seen.
+    auto valu_part = [&](const Step &s) __attribute__((always_inline)) {
+        if (mine(s) && s.sub == 0) {
             m_before = m_run;
             m_tile = -INFINITY;
         }
-
-        if (key0 < N) {
-            // ---- S^T = K Q^T (raw logits, fp32) ----
-            f32x16 S[HK / 32];
-#pragma unroll
-            for (int kb = 0; kb < HK / 32; ++kb) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    S[kb][v] = 0.f;
-                const int kr0 = kb * 32 + lq;
-                const u32x4 *ka = Ks + kr0 * G::CPR;
-                const int ksw = k_swz<D>(kr0);
-#pragma unroll
-                for (int ds = 0; ds < D / 16; ++ds) {
-                    const u32x4 a = ka[(2 * ds + g) ^ ksw];
-                    S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ds], S[kb],
-                                                                    0, 0, 0);
-                }
-            }
-
+        if (act(s)) {
             // keys past the end of the sequence do not exist
-            if (key0 + HK > N) {
+            if (s.key0 + HK > N) {
 #pragma unroll
                 for (int kb = 0; kb < HK / 32; ++kb)
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
-                        if (key0 + kb * 32 + 16 * (v >> 3) + 8 * g + (v & 7) >= N)
+                        if (s.key0 + kb * 32 + 16 * (v >> 3) + 8 * g + (v & 7) >= N)
                             S[kb][v] = -INFINITY;
             }
-
-            // ---- step-local max (log2 units) ----
+            // step-local max (log2 units)
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < HK / 32; ++kb)
@@ -337,8 +523,6 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
             mx = fmaxf(mx, other_half(mx));
             const float m_loc = mx * c2;
             m_tile = fmaxf(m_tile, m_loc);
-
-            // ---- online softmax ----
             // Exponents are taken against the exact running max, so the largest
             // weight of a row is exactly 1 (exact in bf16); O and l are rescaled
             // only when some query's max moved (wave-uniform test).
@@ -346,7 +530,6 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             const float neg = -m_new;
             float rsum = 0.f;
-            bf16x8 P[HK / 16];
 #pragma unroll
             for (int kb = 0; kb < HK / 32; ++kb)
 #pragma unroll
@@ -364,37 +547,90 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
                     for (int v = 0; v < 16; ++v)
                         O[eb][v] *= alpha;
             }
-
-            // ---- O^T += V^T P^T ----
-#pragma unroll
-            for (int eb = 0; eb < D / 32; ++eb) {
-#pragma unroll
-                for (int ks = 0; ks < HK / 16; ++ks) {
-                    const char *va = Vs + (vtr_row + 16 * ks) * G::CPR * 16 + ((eb ^ vtr_seg) * 64) + vtr_col;
-                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va));
-                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va + 4 * G::CPR * 16));
-                    const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    O[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), P[ks], O[eb],
-                                                                    0, 0, 0);
-                }
-            }
         }
-
-        // ---- QK-Skip vote once the whole tile has been seen ----
-        if (vote && sub == SPT - 1) {
+        if (vote && mine(s) && s.sub == SPT - 1) {
             const bool keep_lane = qvalid && !(m_tile - m_before < tau2);
             if (__ballot(keep_lane) != 0ull && lane == 0)
-                atomicOr(&keep[kt >> 5], 1u << (kt & 31));
+                lds_or(&keep[half][s.kt >> 5], 1u << (s.kt & 31));
         }
+    };
 
-        __syncthreads();
-        if (sub_n == 0) {
-            kt = kt_after;
-            kt_after = kt >= 0 ? it.next() : -1;
-        }
-        sub = sub_n;
-        stage ^= 1;
+    Step sp = {-1, 0, 0, 0};  // step u - 1
+    Step sc = gen();          // step u
+    Step sn = gen();          // step u + 1
+    if (half == 0 && loadable(sc)) {
+        const DmaPlan d0 = plan_step(sc, stage0);
+#pragma unroll
+        for (int i = 0; i < G::IPA; ++i)
+            issue_dma(d0, i);
     }
+    __syncthreads();
+
+    // Step u, with its K in stage ST = u mod 3, step u - 1's V in stage
+    // (ST + 2) mod 3 and step u + 1 loading into stage (ST + 1) mod 3.  Each
+    // half runs its own copy of the loop, with the phases in its own order, so
+    // that neither path carries the other's registers; both pass the same
+    // barriers in the same order.  Returns false once both the step and the
+    // one before it are past the end.
+    auto run = [&](auto half_tag) __attribute__((always_inline)) {
+        constexpr int HF = decltype(half_tag)::value;
+        // MFMA phase: PV of step u - 1, then QK^T of step u; the A-waves load
+        // step u + 1 meanwhile.  Without a step u + 1 to load, they reload
+        // step u into the free stage (never read), which keeps the QK^T loop
+        // free of branches.
+        auto mfma_part = [&](const u32x4 *vst, const u32x4 *kst, u32x4 *nst) __attribute__((always_inline)) {
+            if (act(sp))
+                pv_gemm(vst);
+            if (HF == 0) {
+                const bool real = loadable(sn);
+                if (act(sc)) {
+                    s_gemm(kst, plan_step(real ? sn : sc, nst), std::true_type{});
+                } else if (real) {
+                    const DmaPlan d = plan_step(sn, nst);
+#pragma unroll
+                    for (int i = 0; i < G::IPA; ++i)
+                        issue_dma(d, i);
+                }
+            } else if (act(sc)) {
+                s_gemm(kst, plan_step(sc, nst), std::false_type{});
+            }
+        };
+        auto iter = [&](auto stage_tag) __attribute__((always_inline)) -> bool {
+            constexpr int ST = decltype(stage_tag)::value;
+            if (sc.kt < 0 && sp.kt < 0)
+                return false;
+            u32x4 *const kst = ST == 0 ? stage0 : (ST == 1 ? stage1 : stage2);
+            u32x4 *const nst = ST == 0 ? stage1 : (ST == 1 ? stage2 : stage0);
+            u32x4 *const vst = ST == 0 ? stage2 : (ST == 1 ? stage0 : stage1);
+            // phase 1: A computes, B exponentiates; phase 2: the other way round
+            if (HF == 0)
+                mfma_part(vst, kst, nst);
+            else
+                valu_part(sp);
+            __builtin_amdgcn_s_barrier();
+            if (HF == 0)
+                valu_part(sc);
+            else
+                mfma_part(vst, kst, nst);
+            __syncthreads();  // step u + 1 loaded
+            sp = sc;
+            sc = sn;
+            sn = gen();
+            return true;
+        };
+        for (;;) {
+            if (!iter(std::integral_constant<int, 0>{}))
+                break;
+            if (!iter(std::integral_constant<int, 1>{}))
+                break;
+            if (!iter(std::integral_constant<int, 2>{}))
+                break;
+        }
+    };
+    if (half == 0)
+        run(std::integral_constant<int, 0>{});
+    else
+        run(std::integral_constant<int, 1>{});
 
     // ---- epilogue ----
     const float l_tot = l_run + other_half(l_run);
@@ -418,12 +654,16 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     }
     if (vote) {
         __syncthreads();
-        if (tid < W) {
-            uint32_t valid = 0xffffffffu;
-            if (tid == W - 1 && (Tk & 31))
-                valid = (1u << (Tk & 31)) - 1u;
-            const uint32_t in = mrow ? mrow[tid] : 0u;
-            p.mask_out[row * W + tid] = (in | ~keep[tid]) & valid;
+        if (tid < 2 * W) {
+            const int hh = tid / W, w = tid % W;
+            if (hh == 0 || has_b) {
+                const int64_t r = row_a + hh;
+                uint32_t valid = 0xffffffffu;
+                if (w == W - 1 && (Tk & 31))
+                    valid = (1u << (Tk & 31)) - 1u;
+                const uint32_t in = p.mask_in ? p.mask_in[r * W + w] : 0u;
+                p.mask_out[r * W + w] = (in | ~keep[hh][w]) & valid;
+            }
         }
     }
 }
@@ -434,7 +674,12 @@ hipError_t launch(const FwdParams &p, hipStream_t stream)
     const double LOG2E = 1.4426950408889634;
     const float c2 = (float)(p.scale * LOG2E);
     const float tau2 = isinf(p.tau) ? (float)p.tau : (float)(p.tau * LOG2E);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BN>), dim3((unsigned)p.rows), dim3(NT), 0, stream, p, c2, tau2);
+    const int64_t groups = (int64_t)p.B * p.H * ((p.Tq + 1) / 2);
+    if (p.skiplist)
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, true>), dim3((unsigned)groups), dim3(NT), 0, stream, p, c2, tau2);
+    else
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, false>), dim3((unsigned)groups), dim3(NT), 0, stream, p, c2,
+                           tau2);
     return hipGetLastError();
 }
 
