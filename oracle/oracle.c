@@ -33,12 +33,23 @@
  *         Skip-Mask is updated each timestep and marked tiles are bypassed
  *         in subsequent timesteps);
  *       - mask_out = mask_in OR newly-marked: marks are never removed;
- *       - keys >= seqlen do not exist (excluded from every max and sum);
- *         query rows >= seqlen do not vote and are not written;
+ *       - keys >= Nk do not exist (excluded from every max and sum);
+ *         query rows >= Nq do not vote and are not written;
  *       - tau = -inf never marks.
  *
+ *  3. Token ranges ([README] must_do_list / must_skip_list).  Each list holds
+ *     pairs (start_i, end_i) with start_i > end_i, start inclusive and end
+ *     exclusive, in descending order; read literally, pair i covers the key
+ *     tokens t with end_i < t <= start_i.  A key tile
+ *       - is "must-do" when any of its keys lies in a must-do range: it is
+ *         visited whatever mask_in says, and it is never newly marked;
+ *       - is "must-skip" when every one of its keys lies in must-skip ranges
+ *         (and it is not must-do): it is never visited.
+ *     mask_out is still mask_in OR newly-marked.
+ *
  * Inputs are exact upcasts to fp64 of bf16 (raw 16-bit patterns), fp32 or
- * fp64 storage.  q, k, v are BSHD: element (b, n, h, e) at ((b*N + n)*H + h)*D + e.
+ * fp64 storage.  q is BSHD [B][Nq][H][D] and k, v are [B][Nk][H][D]: element
+ * (b, n, h, e) of q at ((b*Nq + n)*H + h)*D + e, of k and v with Nk.
  * Mask rows: W = ceil(Tk/32) uint32 words per row, row id (b*H + h)*Tq + qt,
  * tile kt at word kt/32, bit kt%32; 1 = skip.
  */
@@ -67,14 +78,14 @@ static double elem(const void *p, int dtype, size_t i)
 }
 
 /* s[r][c] = scale * sum_e q[row r][e] * k[key c][e], for one tile */
-static void tile_logits(const void *q, const void *k, int dtype, int N, int H, int D,
+static void tile_logits(const void *q, const void *k, int dtype, int Nq, int Nk, int H, int D,
                         int b, int h, int r0, int nr, int c0, int nc, double scale,
                         double *s /* [nr][nc] */)
 {
     for (int r = 0; r < nr; ++r) {
-        size_t qo = ((size_t)(b * (size_t)N + r0 + r) * H + h) * D;
+        size_t qo = ((size_t)(b * (size_t)Nq + r0 + r) * H + h) * D;
         for (int c = 0; c < nc; ++c) {
-            size_t ko = ((size_t)(b * (size_t)N + c0 + c) * H + h) * D;
+            size_t ko = ((size_t)(b * (size_t)Nk + c0 + c) * H + h) * D;
             double dot = 0.0;
             for (int e = 0; e < D; ++e)
                 dot += elem(q, dtype, qo + e) * elem(k, dtype, ko + e);
@@ -88,24 +99,57 @@ static int is_skipped(const uint32_t *mrow, int kt)
     return mrow ? (int)((mrow[kt >> 5] >> (kt & 31)) & 1u) : 0;
 }
 
+/* key token t lies in one of the n ranges (start_i, end_i): end_i < t <= start_i */
+static int in_ranges(const int32_t *rg, int n, int t)
+{
+    for (int i = 0; i < n; ++i)
+        if (rg[2 * i + 1] < t && t <= rg[2 * i])
+            return 1;
+    return 0;
+}
+
+/* some key of [c0, c0 + nc) is in a must-do range */
+static int tile_must_do(const int32_t *rg, int n, int c0, int nc)
+{
+    for (int t = c0; t < c0 + nc; ++t)
+        if (in_ranges(rg, n, t))
+            return 1;
+    return 0;
+}
+
+/* every key of [c0, c0 + nc) is in a must-skip range */
+static int tile_must_skip(const int32_t *rg, int n, int c0, int nc)
+{
+    if (n <= 0)
+        return 0;
+    for (int t = c0; t < c0 + nc; ++t)
+        if (!in_ranges(rg, n, t))
+            return 0;
+    return 1;
+}
+
 /*
  * oracle_fwd: compute the rows listed in `rows` (row ids as above; NULL = all
- * rows in order).  Outputs are packed per listed row i:
- *   out      [i][BM][D]   (rows >= N left 0)
+ * rows in order).  must_do / must_skip: n_do / n_skip (start, end) pairs, or
+ * NULL.  Outputs are packed per listed row i:
+ *   out      [i][BM][D]   (rows >= Nq left 0)
  *   lse      [i][BM]      (natural log; -inf for a row with no live key)
  *   margin   [i][Tk]      (NaN where the tile was not visited)
  *   mask_out [i][W]       (only when want_mask_out; bits >= Tk are 0)
  * Any output pointer may be NULL.  Returns 0, or -1 on bad arguments.
  */
-int oracle_fwd(int B, int N, int H, int D, int BM, int BN, int dtype,
+int oracle_fwd(int B, int Nq, int Nk, int H, int D, int BM, int BN, int dtype,
                const void *q, const void *k, const void *v,
                const uint32_t *mask_in, int want_mask_out, double tau, double scale,
+               const int32_t *must_do, int n_do, const int32_t *must_skip, int n_skip,
                const int64_t *rows, int64_t nrows,
                double *out, double *lse, double *margin, uint32_t *mask_out, int nthreads)
 {
-    if (B <= 0 || N <= 0 || H <= 0 || D <= 0 || BM <= 0 || BN <= 0 || isnan(tau) || !(scale > 0.0))
+    if (B <= 0 || Nq <= 0 || Nk < 0 || H <= 0 || D <= 0 || BM <= 0 || BN <= 0 || isnan(tau) || !(scale > 0.0))
         return -1;
-    const int Tq = (N + BM - 1) / BM, Tk = (N + BN - 1) / BN, W = (Tk + 31) / 32;
+    if (n_do < 0 || n_skip < 0 || (n_do > 0 && !must_do) || (n_skip > 0 && !must_skip))
+        return -1;
+    const int Tq = (Nq + BM - 1) / BM, Tk = (Nk + BN - 1) / BN, W = (Tk + 31) / 32;
     const int64_t total = (int64_t)B * H * Tq;
     if (!rows)
         nrows = total;
@@ -136,7 +180,7 @@ int oracle_fwd(int B, int N, int H, int D, int BM, int BN, int dtype,
                 continue;
             const int64_t row = rows ? rows[i] : i;
             const int qt = (int)(row % Tq), h = (int)((row / Tq) % H), b = (int)(row / ((int64_t)Tq * H));
-            const int r0 = qt * BM, nr = (N - r0 < BM) ? N - r0 : BM;
+            const int r0 = qt * BM, nr = (Nq - r0 < BM) ? Nq - r0 : BM;
             const uint32_t *mrow = mask_in ? mask_in + row * W : NULL;
 
             /* ---- pass 1: reverse traversal, running max, QK-Skip decisions ---- */
@@ -146,10 +190,11 @@ int oracle_fwd(int B, int N, int H, int D, int BM, int BN, int dtype,
             for (int kt = Tk - 1; kt >= 0; --kt) {
                 if (margin)
                     margin[i * Tk + kt] = NAN;
-                if (is_skipped(mrow, kt))
+                const int c0 = kt * BN, nc = (Nk - c0 < BN) ? Nk - c0 : BN;
+                const int must_do_t = tile_must_do(must_do, n_do, c0, nc);
+                if (!must_do_t && (is_skipped(mrow, kt) || tile_must_skip(must_skip, n_skip, c0, nc)))
                     continue; /* bypassed: no logits, m_run untouched */
-                const int c0 = kt * BN, nc = (N - c0 < BN) ? N - c0 : BN;
-                tile_logits(q, k, dtype, N, H, D, b, h, r0, nr, c0, nc, scale, s);
+                tile_logits(q, k, dtype, Nq, Nk, H, D, b, h, r0, nr, c0, nc, scale, s);
                 double mg = -INFINITY;
                 for (int r = 0; r < nr; ++r) {
                     double mx = -INFINITY;
@@ -163,7 +208,7 @@ int oracle_fwd(int B, int N, int H, int D, int BM, int BN, int dtype,
                 }
                 if (margin)
                     margin[i * Tk + kt] = mg;
-                if (mg < tau)
+                if (mg < tau && !must_do_t)
                     newly[kt >> 5] |= 1u << (kt & 31);
                 for (int r = 0; r < nr; ++r)
                     if (m_loc[r] > m_run[r])
@@ -175,15 +220,16 @@ int oracle_fwd(int B, int N, int H, int D, int BM, int BN, int dtype,
                 l[r] = 0.0;
             memset(acc, 0, sizeof(double) * (size_t)BM * D);
             for (int kt = Tk - 1; kt >= 0; --kt) {
-                if (is_skipped(mrow, kt))
+                const int c0 = kt * BN, nc = (Nk - c0 < BN) ? Nk - c0 : BN;
+                if (!tile_must_do(must_do, n_do, c0, nc) &&
+                    (is_skipped(mrow, kt) || tile_must_skip(must_skip, n_skip, c0, nc)))
                     continue;
-                const int c0 = kt * BN, nc = (N - c0 < BN) ? N - c0 : BN;
-                tile_logits(q, k, dtype, N, H, D, b, h, r0, nr, c0, nc, scale, s);
+                tile_logits(q, k, dtype, Nq, Nk, H, D, b, h, r0, nr, c0, nc, scale, s);
                 for (int r = 0; r < nr; ++r) {
                     for (int c = 0; c < nc; ++c) {
                         double p = exp(s[r * nc + c] - m_run[r]);
                         l[r] += p;
-                        size_t vo = ((size_t)(b * (size_t)N + c0 + c) * H + h) * D;
+                        size_t vo = ((size_t)(b * (size_t)Nk + c0 + c) * H + h) * D;
                         for (int e = 0; e < D; ++e)
                             acc[r * D + e] += p * elem(v, dtype, vo + e);
                     }

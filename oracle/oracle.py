@@ -38,8 +38,10 @@ def bind(path):
     """Load a compiled oracle library (the default one, or a test's variant of it)."""
     lib = ctypes.CDLL(path)
     lib.oracle_fwd.restype = ctypes.c_int
-    lib.oracle_fwd.argtypes = [ctypes.c_int] * 7 + [ctypes.c_void_p] * 4 + [
-        ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_void_p, ctypes.c_int64,
+    lib.oracle_fwd.argtypes = [ctypes.c_int] * 8 + [ctypes.c_void_p] * 4 + [
+        ctypes.c_int, ctypes.c_double, ctypes.c_double,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -80,12 +82,25 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
 
 
+def _ranges(rg):
+    """(start, end) pairs as a flat int32 array and the pair count."""
+    if rg is None or len(rg) == 0:
+        return None, 0
+    a = np.ascontiguousarray(np.asarray(rg, dtype=np.int32).reshape(-1))
+    if a.shape[0] % 2:
+        raise ValueError("a range list holds (start, end) pairs")
+    return a, a.shape[0] // 2
+
+
 def fwd(q, k, v, tile_m, tile_n, tau, scale, mask_in=None, want_mask_out=True, rows=None,
-        nthreads=None, lib=None):
-    """fp64 oracle forward on BSHD q, k, v (torch or numpy; bf16/fp32/fp64).
+        nthreads=None, lib=None, must_do=None, must_skip=None):
+    """fp64 oracle forward on BSHD q [B,Nq,H,D] and k, v [B,Nk,H,D] (torch or numpy;
+    bf16/fp32/fp64).
 
     mask_in: [B*H*Tq, W] words (int32 or uint32) or None (nothing skipped).
     rows:    row ids (b*H + h)*Tq + qt to compute, or None for all rows.
+    must_do, must_skip: flat lists [start_0, end_0, start_1, end_1, ...] of key
+             token ranges ([README] must_do_list / must_skip_list), or None.
     Returns a dict of numpy arrays packed per computed row:
       out [nrows, BM, D], lse [nrows, BM], margin [nrows, Tk] (NaN = not visited),
       mask_out [nrows, W] (uint32), and 'rows'.
@@ -97,9 +112,10 @@ def fwd(q, k, v, tile_m, tile_n, tau, scale, mask_in=None, want_mask_out=True, r
     if not (dt == dk == dv):
         raise TypeError("q, k, v must share a dtype")
     B, N, H, D = qa.shape
-    if ka.shape != qa.shape or va.shape != qa.shape:
+    Nk = ka.shape[1]
+    if ka.shape != (B, Nk, H, D) or va.shape != ka.shape:
         raise ValueError("q, k, v shapes differ")
-    Tq, Tk = -(-N // tile_m), -(-N // tile_n)
+    Tq, Tk = -(-N // tile_m), -(-Nk // tile_n)
     W = -(-Tk // 32)
     if rows is None:
         rows_a = np.arange(B * H * Tq, dtype=np.int64)
@@ -117,8 +133,11 @@ def fwd(q, k, v, tile_m, tile_n, tau, scale, mask_in=None, want_mask_out=True, r
     mask_out = np.zeros((nr, W), np.uint32)
     if nthreads is None:
         nthreads = lib.oracle_max_threads()
-    rc = lib.oracle_fwd(B, N, H, D, tile_m, tile_n, dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(m_in),
-                        int(bool(want_mask_out)), float(tau), float(scale), _ptr(rows_a), nr,
+    do_a, n_do = _ranges(must_do)
+    sk_a, n_sk = _ranges(must_skip)
+    rc = lib.oracle_fwd(B, N, Nk, H, D, tile_m, tile_n, dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(m_in),
+                        int(bool(want_mask_out)), float(tau), float(scale),
+                        _ptr(do_a), n_do, _ptr(sk_a), n_sk, _ptr(rows_a), nr,
                         _ptr(out), _ptr(lse), _ptr(margin), _ptr(mask_out), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_fwd rejected its arguments")
@@ -141,17 +160,80 @@ def unpack_rows(res, B, N, H, tile_m):
     return out[:, :N], lse[:, :, :N]
 
 
-def skiplist(mask, tk):
+def tile_flags(nk, tile_n, must_do=None, must_skip=None):
+    """Per key tile: (must_do, must_skip) booleans from token ranges ([README]
+    must_do_list / must_skip_list: pairs (start, end), start inclusive, end
+    exclusive, descending, so pair i covers tokens end_i < t <= start_i).
+    A tile is must-do when any of its keys is in a must-do range, must-skip
+    when all of its keys are in must-skip ranges."""
+    tk = -(-nk // tile_n)
+    def covered(rg):
+        c = np.zeros(nk, bool)
+        if rg is not None:
+            a = np.asarray(rg, np.int64).reshape(-1, 2)
+            for start, end in a:
+                for t in range(max(end + 1, 0), min(start, nk - 1) + 1):
+                    c[t] = True
+        return c
+    cd, cs = covered(must_do), covered(must_skip)
+    do = np.array([cd[kt * tile_n:(kt + 1) * tile_n].any() for kt in range(tk)], bool)
+    sk = np.array([must_skip is not None and len(must_skip) > 0 and cs[kt * tile_n:(kt + 1) * tile_n].all()
+                   for kt in range(tk)], bool)
+    return do, sk
+
+
+def skiplist(mask, tk, must_do_tiles=None, must_skip_tiles=None):
     """Skip-List of each mask row: [count, live k-tiles in visiting (descending) order].
 
     mask: [rows, W] words; returns (counts [rows] int32, lists: list of int arrays).
-    A tile is live when its bit is clear ([README] QK-Skip: marked tiles are bypassed).
+    A tile is live when its bit is clear ([README] QK-Skip: marked tiles are
+    bypassed), or when it is must-do; must-skip tiles (not must-do) are never live.
+    must_do_tiles / must_skip_tiles: boolean per tile (see tile_flags) or None.
     """
     m = np.asarray(mask).view(np.uint32)
     counts = np.zeros(m.shape[0], np.int32)
     lists = []
     for r in range(m.shape[0]):
-        live = [kt for kt in range(tk - 1, -1, -1) if not (int(m[r, kt // 32]) >> (kt % 32)) & 1]
+        live = []
+        for kt in range(tk - 1, -1, -1):
+            marked = (int(m[r, kt // 32]) >> (kt % 32)) & 1
+            do = must_do_tiles is not None and must_do_tiles[kt]
+            sk = must_skip_tiles is not None and must_skip_tiles[kt]
+            if do or not (marked or sk):
+                live.append(kt)
         counts[r] = len(live)
         lists.append(np.asarray(live, np.int32))
     return counts, lists
+
+
+def merge(outs, lses):
+    """Combine partial attentions over disjoint key sets by their log-sum-exp
+    ([README]: the softmax LSE is returned for combining partial attention
+    results).  outs: list of [..., D] arrays, lses: list of matching [...]
+    arrays (natural log, -inf for a part with no key).  For each query:
+        lse = log(sum_i exp(lse_i)),   out = sum_i exp(lse_i - lse) * out_i
+    with out = 0 and lse = -inf when every part is empty.  fp64."""
+    L = np.stack([np.asarray(x, np.float64) for x in lses])            # [P, ...]
+    O = np.stack([np.asarray(x, np.float64) for x in outs])            # [P, ..., D]
+    m = L.max(axis=0)
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    w = np.exp(L - m_safe)                                              # exp(-inf) = 0
+    s = w.sum(axis=0)
+    lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, s)))
+    out = (w[..., None] * O).sum(axis=0) / np.where(empty, 1.0, s)[..., None]
+    out = np.where(empty[..., None], 0.0, out)
+    return out, lse
+
+
+def error_budgets(num_steps, early_step_ratio=0.3):
+    """Per-timestep error-budget multipliers ([README] "Error Calibration" /
+    "Accumulated-Error Calibration"): for the first floor(T*r) steps the
+    multiplier rises linearly from 0.5 (at step 0) towards 1.0; every later
+    step gets 1.0.  Earlier steps, which weigh more on the final video, get
+    the tighter budgets."""
+    n_early = int(num_steps * early_step_ratio)
+    out = []
+    for t in range(num_steps):
+        out.append(0.5 + 0.5 * (t / n_early) if t < n_early else 1.0)
+    return out

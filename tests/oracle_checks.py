@@ -48,14 +48,16 @@ def to64(x):
 def dense_reference(q, k, v, scale, skip_bits=None, BM=None, BN=None):
     """Brute-force attention with numpy: logits of skipped tiles set to -inf.
 
-    Returns out [B,N,H,D], lse [B,H,N] and the probabilities [B,H,N,N]."""
+    q [B,Nq,H,D], k and v [B,Nk,H,D].  Returns out [B,Nq,H,D], lse [B,H,Nq]
+    and the probabilities [B,H,Nq,Nk]."""
     q, k, v = to64(q), to64(k), to64(v)
     B, N, H, D = q.shape
+    Nk = k.shape[1]
     s = scale * np.einsum("bnhe,bmhe->bhnm", q, k)
     if skip_bits is not None:
-        Tq, Tk = -(-N // BM), -(-N // BN)
-        sb = skip_bits.reshape(B, H, Tq, Tk)
-        full = np.repeat(np.repeat(sb, BM, axis=2), BN, axis=3)[:, :, :N, :N]
+        Tq, Tk = -(-N // BM), -(-Nk // BN)
+        sb = np.asarray(skip_bits).reshape(B, H, Tq, Tk)
+        full = np.repeat(np.repeat(sb, BM, axis=2), BN, axis=3)[:, :, :N, :Nk]
         s = np.where(full, -np.inf, s)
     m = s.max(axis=-1, keepdims=True)
     mf = np.where(np.isfinite(m), m, 0.0)
@@ -262,4 +264,90 @@ def check_edge_cases(lib=None):
     return fails
 
 
-ALL_CHECKS = (run_golden, check_dense, check_masked_and_rule, check_tile_invariance, check_edge_cases)
+def check_nonsquare(lib=None):
+    """Queries and keys of different lengths (the text/video partial attentions
+    and K/V splits of the pages): plain and masked attention, by brute force."""
+    fails = []
+    for seed, B, Nq, Nk, H, D, BM, BN in ((0, 1, 20, 53, 2, 8, 8, 16), (1, 2, 61, 9, 1, 4, 16, 4),
+                                          (2, 1, 7, 100, 1, 8, 4, 32)):
+        g = torch.Generator().manual_seed(300 + seed)
+        q = 1.5 * torch.randn(B, Nq, H, D, generator=g, dtype=torch.float64)
+        k = 1.5 * torch.randn(B, Nk, H, D, generator=g, dtype=torch.float64)
+        v = torch.randn(B, Nk, H, D, generator=g, dtype=torch.float64)
+        scale = 1.0 / math.sqrt(D)
+        Tq, Tk = -(-Nq // BM), -(-Nk // BN)
+        rng = np.random.default_rng(seed)
+        for bits in (None, rng.random((B * H * Tq, Tk)) < 0.3):
+            r = oracle.fwd(q, k, v, BM, BN, -2.0, scale, mask_in=None if bits is None else words_of(bits), lib=lib)
+            o, lse = oracle.unpack_rows(r, B, Nq, H, BM)
+            o_ref, lse_ref, _ = dense_reference(q, k, v, scale, bits, BM, BN)
+            if not np.allclose(o, o_ref, atol=1e-12, rtol=1e-12):
+                fails.append("non-square out case %d (masked=%s)" % (seed, bits is not None))
+            fin = np.isfinite(lse_ref)
+            if not (np.array_equal(fin, np.isfinite(lse)) and np.allclose(lse[fin], lse_ref[fin], atol=1e-12)):
+                fails.append("non-square lse case %d" % seed)
+    return fails
+
+
+def load_range_golden():
+    with open(os.path.join(GOLDEN, "token_ranges_examples.json")) as f:
+        return json.load(f)
+
+
+def check_ranges(lib=None):
+    """must_do_list / must_skip_list: the hand-derived tile sets of the pages'
+    examples, the output as brute-force attention over the visited tiles, and
+    the rule that must-do tiles are never marked."""
+    fails = []
+    doc = load_range_golden()
+    rng = np.random.default_rng(7)
+    for case in doc["cases"]:
+        N, BN = case["N"], case["BN"]
+        Tk = -(-N // BN)
+        BM = 8
+        Tq = -(-N // BM)
+        g = torch.Generator().manual_seed(len(case["name"]))
+        q = 2.0 * torch.randn(1, N, 1, 8, generator=g, dtype=torch.float64)
+        k = 2.0 * torch.randn(1, N, 1, 8, generator=g, dtype=torch.float64)
+        v = torch.randn(1, N, 1, 8, generator=g, dtype=torch.float64)
+        do_t = np.zeros(Tk, bool)
+        do_t[case.get("must_do_tiles", [])] = True
+        sk_t = np.zeros(Tk, bool)
+        sk_t[case.get("must_skip_tiles", [])] = True
+        for mask_kind in ("empty", "random", "full"):
+            if mask_kind == "empty":
+                bits = np.zeros((Tq, Tk), bool)
+            elif mask_kind == "full":
+                bits = np.ones((Tq, Tk), bool)
+            else:
+                bits = rng.random((Tq, Tk)) < 0.4
+            for tau in (-math.inf, -1.0, 1e30):
+                r = oracle.fwd(q, k, v, BM, BN, tau, 0.4, mask_in=words_of(bits), lib=lib,
+                               must_do=case.get("must_do"), must_skip=case.get("must_skip"))
+                eff = (bits | sk_t[None, :]) & ~do_t[None, :]
+                o, _ = oracle.unpack_rows(r, 1, N, 1, BM)
+                o_ref, _, _ = dense_reference(q, k, v, 0.4, eff, BM, BN)
+                if not np.allclose(o, o_ref, atol=1e-12):
+                    fails.append("%s (%s mask, tau %g): output is not attention over the visited tiles"
+                                 % (case["name"], mask_kind, tau))
+                out_bits = bits_of(r["mask_out"], Tk)
+                newly = out_bits & ~bits
+                if np.any(newly & do_t[None, :]):
+                    fails.append("%s: a must-do tile was marked" % case["name"])
+                if np.any(newly & eff):
+                    fails.append("%s: a tile that was not visited was marked" % case["name"])
+                if np.any(bits & ~out_bits):
+                    fails.append("%s: an input mark was dropped" % case["name"])
+                if tau == 1e30:
+                    # every visited tile but the first of its row and the must-do ones is marked
+                    for row in range(Tq):
+                        vis = [kt for kt in range(Tk - 1, -1, -1) if not eff[row, kt]]
+                        want = set(kt for kt in vis[1:] if not do_t[kt])
+                        if set(np.flatnonzero(newly[row]).tolist()) != want:
+                            fails.append("%s: marks at tau=+big, row %d" % (case["name"], row))
+                            break
+    return fails
+
+
+ALL_CHECKS = (run_golden, check_dense, check_masked_and_rule, check_tile_invariance, check_edge_cases,
+              check_nonsquare, check_ranges)

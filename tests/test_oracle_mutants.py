@@ -19,26 +19,35 @@ MUTANTS = [
     ("any row passes", "if (d > mg)\n                        mg = d;",
      "if (mg == -INFINITY || d < mg)\n                        mg = d;"),
     ("sign flipped", "double d = mx - m_run[r];", "double d = m_run[r] - mx;"),
-    ("non-strict test", "if (mg < tau)", "if (mg <= tau)"),
+    ("non-strict test", "if (mg < tau && !must_do_t)", "if (mg <= tau && !must_do_t)"),
     ("missing keys as zero logits", "m_loc[r] = mx;", "m_loc[r] = (nc < BN && mx < 0.0) ? 0.0 : mx;"),
     ("missing rows vote", "if (margin)\n                    margin[i * Tk + kt] = mg;",
      "if (nr < BM && mg < 0.0)\n                    mg = 0.0;\n                if (margin)\n                    margin[i * Tk + kt] = mg;"),
     ("scale dropped", "s[r * nc + c] = scale * dot;", "s[r * nc + c] = dot;"),
     ("q used as k", "dot += elem(q, dtype, qo + e) * elem(k, dtype, ko + e);",
      "dot += elem(q, dtype, qo + e) * elem(q, dtype, ko + e);"),
-    ("wrong head of k", "size_t ko = ((size_t)(b * (size_t)N + c0 + c) * H + h) * D;",
-     "size_t ko = ((size_t)(b * (size_t)N + c0 + c) * H + 0) * D;"),
+    ("wrong head of k", "size_t ko = ((size_t)(b * (size_t)Nk + c0 + c) * H + h) * D;",
+     "size_t ko = ((size_t)(b * (size_t)Nk + c0 + c) * H + 0) * D;"),
+    ("k indexed with the query length", "size_t ko = ((size_t)(b * (size_t)Nk + c0 + c) * H + h) * D;",
+     "size_t ko = ((size_t)(b * (size_t)Nq + c0 + c) * H + h) * D;"),
     ("no normalisation", "valid ? acc[r * D + e] / l[r] : 0.0", "valid ? acc[r * D + e] : 0.0"),
     ("mask_in not kept", "(in | nw) & keep_bits", "(nw) & keep_bits"),
     ("padding bits kept", "(in | nw) & keep_bits", "(in | nw)"),
-    ("marked tile dropped at once", "for (int kt = Tk - 1; kt >= 0; --kt) {\n                if (is_skipped(mrow, kt))\n                    continue;\n                const int c0 = kt * BN, nc = (N - c0 < BN) ? N - c0 : BN;\n                tile_logits(q, k, dtype, N, H, D, b, h, r0, nr, c0, nc, scale, s);\n                for (int r = 0; r < nr; ++r) {\n                    for (int c = 0; c < nc; ++c) {",
-     "for (int kt = Tk - 1; kt >= 0; --kt) {\n                if (is_skipped(mrow, kt) || ((newly[kt >> 5] >> (kt & 31)) & 1u))\n                    continue;\n                const int c0 = kt * BN, nc = (N - c0 < BN) ? N - c0 : BN;\n                tile_logits(q, k, dtype, N, H, D, b, h, r0, nr, c0, nc, scale, s);\n                for (int r = 0; r < nr; ++r) {\n                    for (int c = 0; c < nc; ++c) {"),
+    ("marked tile dropped at once", "                if (!tile_must_do(must_do, n_do, c0, nc) &&\n                    (is_skipped(mrow, kt) || tile_must_skip(must_skip, n_skip, c0, nc)))\n                    continue;\n                tile_logits(",
+     "                if (!tile_must_do(must_do, n_do, c0, nc) &&\n                    (is_skipped(mrow, kt) || tile_must_skip(must_skip, n_skip, c0, nc) || ((newly[kt >> 5] >> (kt & 31)) & 1u)))\n                    continue;\n                tile_logits("),
     ("running max frozen at first tile", "if (m_loc[r] > m_run[r])\n                        m_run[r] = m_loc[r];",
      "if (m_run[r] == -INFINITY)\n                        m_run[r] = m_loc[r];"),
     ("lse without max", "lse[i * BM + r] = valid ? m_run[r] + log(l[r]) : -INFINITY;",
      "lse[i * BM + r] = valid ? log(l[r]) : -INFINITY;"),
-    ("v from wrong row", "size_t vo = ((size_t)(b * (size_t)N + c0 + c) * H + h) * D;",
-     "size_t vo = ((size_t)(b * (size_t)N + c0 + (nc - 1 - c)) * H + h) * D;"),
+    ("v from wrong row", "size_t vo = ((size_t)(b * (size_t)Nk + c0 + c) * H + h) * D;",
+     "size_t vo = ((size_t)(b * (size_t)Nk + c0 + (nc - 1 - c)) * H + h) * D;"),
+    ("range end inclusive", "if (rg[2 * i + 1] < t && t <= rg[2 * i])", "if (rg[2 * i + 1] <= t && t <= rg[2 * i])"),
+    ("range start exclusive", "if (rg[2 * i + 1] < t && t <= rg[2 * i])", "if (rg[2 * i + 1] < t && t < rg[2 * i])"),
+    ("must-skip on any key", "        if (!in_ranges(rg, n, t))\n            return 0;\n    return 1;",
+     "        if (in_ranges(rg, n, t))\n            return 1;\n    return 0;"),
+    ("must-do tiles may be marked", "if (mg < tau && !must_do_t)", "if (mg < tau)"),
+    ("must-do does not override the mask", "if (!must_do_t && (is_skipped(mrow, kt) || tile_must_skip(must_skip, n_skip, c0, nc)))",
+     "if (is_skipped(mrow, kt) || (!must_do_t && tile_must_skip(must_skip, n_skip, c0, nc)))"),
 ]
 
 

@@ -157,3 +157,77 @@ def test_c1_trajectory_masks_grow_and_stay_nondegenerate():
 
 def test_edge_case_checks():
     assert oc.check_edge_cases() == []
+
+
+def test_queries_and_keys_of_different_lengths():
+    assert oc.check_nonsquare() == []
+
+
+def test_must_do_and_must_skip_ranges():
+    assert oc.check_ranges() == []
+
+
+def test_tile_flags_match_the_hand_derived_examples():
+    """The Python tile-flag helper (used by the Skip-List reference) gives the
+    tile sets derived by hand from the README's examples."""
+    for case in oc.load_range_golden()["cases"]:
+        do, sk = oracle.tile_flags(case["N"], case["BN"], case.get("must_do"), case.get("must_skip"))
+        assert np.flatnonzero(do).tolist() == case.get("must_do_tiles", []), case["name"]
+        assert np.flatnonzero(sk).tolist() == case.get("must_skip_tiles", []), case["name"]
+
+
+def test_skiplist_reference_with_ranges():
+    do = np.array([True, False, False, True, False])
+    sk = np.array([False, True, False, True, False])
+    bits = np.array([[1, 0, 0, 1, 0], [0, 0, 1, 0, 1]], bool)
+    counts, lists = oracle.skiplist(oc.words_of(bits), 5, do, sk)
+    assert list(lists[0]) == [4, 3, 2, 0]     # 3 must-do beats its mark and must-skip; 1 must-skip
+    assert list(lists[1]) == [3, 0]           # 4 and 2 marked, 1 must-skip
+    assert list(counts) == [4, 2]
+
+
+def test_lse_merge_of_key_splits_is_full_attention():
+    """Attention over a partition of the keys, merged by LSE, is attention over
+    all keys -- by brute force; also through the oracle's own forward on the
+    K/V splits (the sequence-parallel use), with a part left empty."""
+    g = torch.Generator().manual_seed(21)
+    B, Nq, Nk, H, D = 2, 30, 70, 2, 8
+    q = 1.5 * torch.randn(B, Nq, H, D, generator=g, dtype=torch.float64)
+    k = 1.5 * torch.randn(B, Nk, H, D, generator=g, dtype=torch.float64)
+    v = torch.randn(B, Nk, H, D, generator=g, dtype=torch.float64)
+    scale = 0.4
+    o_ref, lse_ref, _ = oc.dense_reference(q, k, v, scale)
+    cuts = [0, 16, 17, 48, 70]
+    outs, lses = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        o, lse, _ = oc.dense_reference(q, k[:, a:b], v[:, a:b], scale)
+        outs.append(o)
+        lses.append(np.transpose(lse, (0, 2, 1)))          # [B, Nq, H] to match out[..., :]
+    out, lse = oracle.merge(outs, lses)
+    assert np.allclose(out, o_ref, atol=1e-12) and np.allclose(lse, np.transpose(lse_ref, (0, 2, 1)), atol=1e-12)
+    # through the oracle forward, per split, with an empty split
+    outs, lses = [], []
+    for a, b in ((0, 32), (32, 32), (32, 70)):
+        r = oracle.fwd(q, k[:, a:b], v[:, a:b], 8, 16, -math.inf, scale)
+        o, l = oracle.unpack_rows(r, B, Nq, H, 8)
+        outs.append(o)
+        lses.append(np.transpose(l, (0, 2, 1)))
+    out, lse = oracle.merge(outs, lses)
+    assert np.allclose(out, o_ref, atol=1e-12)
+    # every part empty: 0 and -inf
+    out, lse = oracle.merge([np.ones((3, 4))] * 2, [np.full(3, -np.inf)] * 2)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_error_budgets_follow_the_printed_schedule():
+    """[README] Error Calibration: over the first int(T*ratio) steps the
+    multiplier goes 0.5 + 0.5*t/int(T*ratio); later steps get 1.0."""
+    b = oracle.error_budgets(50, 0.3)
+    assert len(b) == 50
+    assert b[0] == 0.5
+    assert b[1] == 0.5 + 0.5 / 15
+    assert b[14] == 0.5 + 0.5 * 14 / 15
+    assert all(x == 1.0 for x in b[15:])
+    assert b[:15] == sorted(b[:15])
+    assert oracle.error_budgets(3, 0.3) == [1.0, 1.0, 1.0]    # int(0.9) = 0 early steps
+    assert oracle.error_budgets(10, 0.5)[:5] == [0.5, 0.6, 0.7, 0.8, 0.9]
