@@ -6,8 +6,10 @@
  *   [README]   LiteAttention project README (moonmath-ai/LiteAttention):
  *              "QK-Skip Algorithm", "Full-Stage Elimination", the threshold
  *              ablation table, the Python API (threshold, reset of the skip
- *              state, turning skipping off, must-do list note that the kernel
- *              iterates in reverse order, LSE return) and the debug flags.
+ *              state, turning skipping off, must_do_list / must_skip_list and
+ *              the note that the kernel iterates in reverse order,
+ *              SeqParallelLiteAttention with split_idx, LSE return and the
+ *              text/video partial-attention example) and the debug flags.
  *   [ABSTRACT] "LiteAttention: A Temporal Sparse Attention for Diffusion
  *              Transformers", arXiv 2511.11062, abstract.
  *   [SKILL]    "Lite Attention Temporal Sparse" skill page: Skip-Mask as a
@@ -16,12 +18,16 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * - Tensors are BSHD and contiguous: element (b, n, h, e) of q, k, v and out
- *   sits at ((b*seqlen + n)*heads + h)*head_dim + e.  [README] Wan
- *   integration: the attention takes (batch, seq_len, heads, head_dim) and
- *   returns (batch, seq_len, heads*head_dim) -- the same bytes.
+ * - Tensors are BSHD: element (n, h, e) of batch entry b of q sits at
+ *   b*q_batch_stride + (n*heads + h)*head_dim + e, of out at
+ *   b*out_batch_stride + ..., and of k and v at b*kv_batch_stride + ....
+ *   With zero strides the tensors are contiguous [B][seqlen][H][d] and
+ *   [B][seqlen_kv][H][d]; a non-zero stride passes a slice along the sequence
+ *   of a larger tensor without a copy (the [README] text/video split,
+ *   q[:, :text_len], and the K/V splits of SeqParallelLiteAttention).  [README] Wan integration: the
+ *   attention takes (batch, seq_len, heads, head_dim).
  * - Tiles: a q-tile is tile_m consecutive query tokens, a k-tile tile_n
- *   consecutive key tokens.  Tq = ceil(seqlen/tile_m), Tk = ceil(seqlen/tile_n).
+ *   consecutive key tokens.  Tq = ceil(seqlen/tile_m), Tk = ceil(seqlen_kv/tile_n).
  *   A "row" is one (b, h, q-tile); row id = (b*heads + h)*Tq + qt.
  * - Skip-Mask (the persistent per-layer state, [README] QK-Skip Algorithm):
  *   W = ceil(Tk/32) uint32 words per row, row-major; k-tile kt of a row is
@@ -30,6 +36,13 @@
  * - Skip-List ([SKILL]): int32 per row, stride 1 + Tk: element 0 is the
  *   number of live k-tiles L, elements 1..L are the live k-tiles in the order
  *   the forward visits them (descending).  Elements after L are not written.
+ * - Token ranges ([README] must_do_list / must_skip_list): pairs (start, end)
+ *   of key token indices, start inclusive and end exclusive, listed in
+ *   descending order because the kernel iterates in reverse: pair i covers
+ *   the keys t with end_i < t <= start_i.  A k-tile holding any must-do key
+ *   is visited whatever the mask says and is never marked; a k-tile whose
+ *   keys all lie in must-skip ranges (and that is not must-do) is never
+ *   visited.  Ranges are the same for every row.
  * - Device pointers are plain HIP device addresses owned by the caller; the
  *   library allocates nothing, keeps no pointer and no state between calls,
  *   and is reentrant.  `stream` is a hipStream_t (NULL = the null stream).
@@ -39,7 +52,8 @@
  *   lite_attn_strerror gives its text (for LITE_ERR_HIP, with the HIP error
  *   of the failing call of this thread).
  * - A descriptor with batch, seqlen or heads equal to 0 describes empty
- *   tensors: the call validates the rest and does nothing.
+ *   tensors: the call validates the rest and does nothing.  seqlen_kv = 0
+ *   with queries present gives every query no key: out 0, lse -inf.
  */
 #ifndef LITE_ATTN_H
 #define LITE_ATTN_H
@@ -51,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LITE_ATTN_ABI_VERSION 1
+#define LITE_ATTN_ABI_VERSION 2
 
 typedef enum {
     LITE_BF16 = 0, /* bf16 q, k, v, out; fp32 accumulation */
@@ -59,31 +73,45 @@ typedef enum {
 } lite_attn_dtype;
 
 typedef struct {
-    int32_t batch;    /* B >= 0 */
-    int32_t seqlen;   /* N >= 0, any value (the last tiles may be partial) */
-    int32_t heads;    /* H >= 0 */
-    int32_t head_dim; /* d */
-    int32_t tile_m;   /* BM: query rows per tile */
-    int32_t tile_n;   /* BN: key columns per tile */
-    int32_t dtype;    /* lite_attn_dtype */
+    int32_t batch;           /* B >= 0 */
+    int32_t seqlen;          /* Nq >= 0 queries per batch entry (the last tiles may be partial) */
+    int32_t heads;           /* H >= 0 */
+    int32_t head_dim;        /* d */
+    int32_t tile_m;          /* BM: query rows per tile */
+    int32_t tile_n;          /* BN: key columns per tile */
+    int32_t dtype;           /* lite_attn_dtype */
+    int32_t seqlen_kv;       /* Nk >= 0 keys (and values) per batch entry */
+    int64_t q_batch_stride;  /* elements between batch entries of q and out; 0 = seqlen*heads*head_dim */
+    int64_t kv_batch_stride; /* elements between batch entries of k and v; 0 = seqlen_kv*heads*head_dim */
+    int64_t out_batch_stride; /* elements between batch entries of out; 0 = seqlen*heads*head_dim */
 } lite_attn_desc;
+
+/* must-do / must-skip key token ranges (host memory, read during the call). */
+typedef struct {
+    const int32_t *must_do;   /* 2*n_must_do values: start_0, end_0, start_1, end_1, ...; NULL if n is 0 */
+    int32_t n_must_do;        /* number of (start, end) pairs, >= 0 */
+    const int32_t *must_skip; /* same convention */
+    int32_t n_must_skip;
+} lite_attn_ranges;
 
 /* Supported (dtype, head_dim, tile_m x tile_n):
  *   LITE_BF16: head_dim 64 or 128; tile 128x64 or 128x128.
  *   LITE_FP32: head_dim 64; tile 64x64.
  * Anything else is LITE_ERR_UNSUPPORTED (never a silent fallback).
- * Tk may be at most 4096. */
+ * Tk may be at most 4096.  lite_attn_merge takes head_dim 8, 16, 32, 64,
+ * 128, 256 or 512, in either dtype. */
 
 enum {
     LITE_OK = 0,
     LITE_ERR_NULL_ARG = 1,      /* a required pointer is NULL */
-    LITE_ERR_BAD_SHAPE = 2,     /* negative size, or sizes overflow */
-    LITE_ERR_UNSUPPORTED = 3,   /* (dtype, head_dim, tile) not built, or Tk too large */
+    LITE_ERR_BAD_SHAPE = 2,     /* negative size or stride, batch entries overlapping, or sizes overflow */
+    LITE_ERR_UNSUPPORTED = 3,   /* (dtype, head_dim, tile) not built, Tk too large, too many merge parts */
     LITE_ERR_BAD_THRESHOLD = 4, /* tau is NaN, or > 0 without LITE_ATTENTION_DEBUG */
     LITE_ERR_BAD_SCALE = 5,     /* softmax_scale not finite and > 0 */
-    LITE_ERR_MISALIGNED = 6,    /* q/k/v/out not 16-byte, mask/skiplist/lse not 4-byte aligned */
+    LITE_ERR_MISALIGNED = 6,    /* q/k/v/out or a batch stride not 16-byte, mask/skiplist/lse not 4-byte */
     LITE_ERR_ALIAS = 7,         /* out or lse overlaps an input; mask_out partly overlaps mask_in */
-    LITE_ERR_HIP = 8            /* a HIP call failed (launch or device query) */
+    LITE_ERR_HIP = 8,           /* a HIP call failed (launch or device query) */
+    LITE_ERR_BAD_RANGES = 9     /* a token range list is malformed (see the conventions above) */
 };
 
 /* Words of one Skip-Mask for all rows: B*H*Tq*ceil(Tk/32).  0 for a bad descriptor. */
@@ -109,7 +137,8 @@ size_t lite_attn_skiplist_len(const lite_attn_desc *desc);
  * marked tile still counts in this call's output and is skipped from the
  * next call on (the mask carried to the next denoising step).
  *
- *   q, k, v   device, [B][N][H][d] of dtype, 16-byte aligned; read only.
+ *   q, k, v   device, of dtype, laid out as in the conventions, 16-byte
+ *             aligned; read only.  k and v may be NULL when seqlen_kv is 0.
  *   mask_in   device, lite_attn_mask_words() uint32; NULL = nothing skipped
  *             (the "skipping off" path of the [README] API: plain attention).
  *   mask_out  device, same size; NULL = no marking.  Receives
@@ -119,31 +148,38 @@ size_t lite_attn_skiplist_len(const lite_attn_desc *desc);
  *   skiplist  device, lite_attn_skiplist_len() int32, or NULL.  When given,
  *             the live tiles are read from it instead of from mask_in; it
  *             must have been built by lite_attn_build_skiplist from this
- *             mask_in (mask_in is still read for mask_out).
+ *             mask_in with the same ranges (mask_in is still read for
+ *             mask_out).
  *   tau       threshold in natural-log units.  -inf never marks.  NaN is
  *             LITE_ERR_BAD_THRESHOLD; tau > 0 is too unless the environment
  *             variable LITE_ATTENTION_DEBUG is set to anything other than
  *             "FALSE" ([README] debug flags).
  *   softmax_scale  multiplier of q.k; finite and > 0 (1/sqrt(d) is usual).
- *   out       device, [B][N][H][d] of dtype, 16-byte aligned; written for
- *             every query.  A query whose row has no live tile gets 0.
- *   lse       device, fp32 [B][H][N], or NULL: natural-log log-sum-exp of the
- *             query's live logits ([README]: softmax LSE for merging partial
- *             attentions); -inf when the row has no live tile.
+ *   out       device, [B][seqlen][H][d] with out_batch_stride, 16-byte
+ *             aligned; written for every query.  A query whose row has no
+ *             live tile gets 0.
+ *   lse       device, fp32 [B][H][seqlen] contiguous, or NULL: natural-log
+ *             log-sum-exp of the query's live logits ([README]: softmax LSE
+ *             for merging partial attentions); -inf when the row has no live
+ *             tile.
+ *   ranges    host, or NULL for none: must-do / must-skip key ranges.
  *   stream    hipStream_t.
  */
 int lite_attn_fwd(const lite_attn_desc *desc, const void *q, const void *k, const void *v,
                   const uint32_t *mask_in, uint32_t *mask_out, const int32_t *skiplist,
-                  float tau, float softmax_scale, void *out, float *lse, void *stream);
+                  float tau, float softmax_scale, void *out, float *lse, const lite_attn_ranges *ranges,
+                  void *stream);
 
 /*
  * lite_attn_build_skiplist -- compact each row of a Skip-Mask into its
- * Skip-List ([SKILL] "Skip-List for high sparsity").
+ * Skip-List ([SKILL] "Skip-List for high sparsity"): the tiles the forward
+ * would visit under this mask and these ranges, in visiting order.
  *   mask      device, lite_attn_mask_words() uint32 (NULL = nothing skipped).
  *   skiplist  device, lite_attn_skiplist_len() int32; must not overlap mask.
+ *   ranges    host, or NULL: the ranges the forward will be called with.
  */
 int lite_attn_build_skiplist(const lite_attn_desc *desc, const uint32_t *mask, int32_t *skiplist,
-                             void *stream);
+                             const lite_attn_ranges *ranges, void *stream);
 
 /*
  * lite_attn_reset_mask -- clear a Skip-Mask: every tile live again ([README]
@@ -152,6 +188,31 @@ int lite_attn_build_skiplist(const lite_attn_desc *desc, const uint32_t *mask, i
  *   mask      device, lite_attn_mask_words() uint32.
  */
 int lite_attn_reset_mask(const lite_attn_desc *desc, uint32_t *mask, void *stream);
+
+/* Most partial attentions one lite_attn_merge call combines. */
+#define LITE_ATTN_MAX_MERGE_PARTS 8
+
+/*
+ * lite_attn_merge -- combine partial attentions of the same queries over
+ * disjoint key sets into the attention over their union ([README]: the
+ * softmax LSE is returned "for combining results from multiple partial
+ * attention computations" -- the text/video split and the K/V splits of
+ * SeqParallelLiteAttention).  For every query (b, n, h):
+ *     lse = ln(sum_i exp(lse_i)),   out = sum_i exp(lse_i - lse) * out_i,
+ * computed in fp32; a part with lse_i = -inf (no key) contributes nothing;
+ * when every part has -inf the query gets out 0 and lse -inf.
+ *   desc      batch, seqlen (queries), heads, head_dim and dtype; every
+ *             out_i has batch stride q_batch_stride, out has
+ *             out_batch_stride; tiles and seqlen_kv are not used.
+ *   nparts    1..LITE_ATTN_MAX_MERGE_PARTS.
+ *   outs      host array of nparts device pointers, 16-byte aligned.
+ *   lses      host array of nparts device pointers, fp32 [B][H][seqlen].
+ *   out       device.  May be exactly one of outs when the two strides are
+ *             equal (in place); any other overlap is LITE_ERR_ALIAS.
+ *   lse       device, fp32 [B][H][seqlen], or NULL.  May be exactly one of lses.
+ */
+int lite_attn_merge(const lite_attn_desc *desc, int32_t nparts, const void *const *outs,
+                    const float *const *lses, void *out, float *lse, void *stream);
 
 /* Text of a return code.  For LITE_ERR_HIP it includes the HIP error text of
  * this thread's last failing call.  Never NULL. */

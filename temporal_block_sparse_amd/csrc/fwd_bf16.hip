@@ -126,7 +126,9 @@ struct LiveTiles {
     int cnt, idx;
     bool none;
 
-    __device__ __forceinline__ void init(const uint32_t *m, const int32_t *l, int tk, bool exists)
+    // rdo[j] / rsk[j]: must-do / must-skip tile bits of word lane + 64*j
+    __device__ __forceinline__ void init(const uint32_t *m, const int32_t *l, int tk, bool exists,
+                                         const uint32_t (&rdo)[2], const uint32_t (&rsk)[2])
     {
         const int lane = threadIdx.x & 63;
         none = !exists;
@@ -146,16 +148,17 @@ struct LiveTiles {
             chunk = lane < cnt ? l[1 + lane] : -1;
         } else {
             const int W = (tk + 31) >> 5;
-            auto live = [&](int wi) -> uint32_t {
+            auto live = [&](int wi, int j) -> uint32_t {
                 if (wi >= W)
                     return 0u;
                 uint32_t bits = m ? ~m[wi] : 0xffffffffu;
+                bits = (bits & ~rsk[j]) | rdo[j];
                 if (wi == W - 1 && (tk & 31))
                     bits &= (1u << (tk & 31)) - 1u;
                 return bits;
             };
-            wlo = live(lane);
-            whi = live(lane + 64);
+            wlo = live(lane, 0);
+            whi = live(lane + 64, 1);
             nzlo = __ballot(wlo != 0u);
             nzhi = __ballot(whi != 0u);
             w = W;
@@ -209,10 +212,11 @@ struct LivePair {
     LiveTiles<LIST> a, b;
     int na, nb;
     __device__ __forceinline__ void init(const uint32_t *ma, const int32_t *la, const uint32_t *mb,
-                                         const int32_t *lb, int tk, bool has_b)
+                                         const int32_t *lb, int tk, bool has_b, const uint32_t (&rdo)[2],
+                                         const uint32_t (&rsk)[2])
     {
-        a.init(ma, la, tk, true);
-        b.init(mb, lb, tk, has_b);
+        a.init(ma, la, tk, true, rdo, rsk);
+        b.init(mb, lb, tk, has_b, rdo, rsk);
         na = a.next(tk);
         nb = b.next(tk);
     }
@@ -296,7 +300,7 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     const int half = wave >> 2;                                 // 0: q-tile A, 1: q-tile B
     const int wq = wave & 3;                                    // 32-query block in the q-tile
     const int g = lane >> 5, lq = lane & 31;
-    const int N = p.N, H = p.H, Tq = p.Tq, Tk = p.Tk, W = p.W;
+    const int Nq = p.Nq, Nk = p.Nk, H = p.H, Tq = p.Tq, Tk = p.Tk, W = p.W;
     const int Tq2 = (Tq + 1) >> 1;
     const int pq = (int)(blockIdx.x % Tq2);
     const int64_t bh = blockIdx.x / Tq2;
@@ -306,18 +310,22 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     const int qt = 2 * pq + half;            // this wave's q-tile
     const int rs = H * D;                    // token stride (elements)
     const int rs2 = rs * 2;                  // token stride (bytes)
-    const int64_t base = (int64_t)b * N * rs + (int64_t)h * D;
-    const __bf16 *Qb = (const __bf16 *)p.q + base;
-    const char *Kb = (const char *)((const __bf16 *)p.k + base);
-    const char *Vb = (const char *)((const __bf16 *)p.v + base);
+    const int64_t qbase = (int64_t)b * p.q_sb + (int64_t)h * D;
+    const int64_t kvbase = (int64_t)b * p.kv_sb + (int64_t)h * D;
+    const __bf16 *Qb = (const __bf16 *)p.q + qbase;
+    const char *Kb = (const char *)((const __bf16 *)p.k + kvbase);
+    const char *Vb = (const char *)((const __bf16 *)p.v + kvbase);
     const bool vote = p.mask_out != nullptr;
+    const bool ranges = p.rg.any != 0;
 
+    // keep-vector: a clear bit marks the tile in mask_out.  Must-skip tiles are
+    // never visited and never marked, so their bits start set.
     if (tid < 2 * W)
-        keep[tid / W][tid % W] = 0u;
+        keep[tid / W][tid % W] = ranges ? p.rg.skip_bits[tid % W] : 0u;
 
     // this lane's query and its Q^T B-operand fragments
     const int qi = qt * BM + wq * 32 + lq;
-    const bool qvalid = qt < Tq && qi < N;
+    const bool qvalid = qt < Tq && qi < Nq;
     bf16x8 qf[D / 16];
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
@@ -343,12 +351,12 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         vgo[i] = lr * rs2 + (pos ^ v_swz<D>(lr)) * 16;
     }
     // The loads of one step into one LDS stage.  Rows past the end of the
-    // sequence are clamped to key N-1 (their logits are set to -inf before
+    // sequence are clamped to key Nk-1 (their logits are set to -inf before
     // use), so every address is in bounds.
     struct DmaPlan {
         const char *kb, *vb;
         char *kdst, *vdst;
-        int over;  // first key - (N - 1): row r is clamped when r + over > 0
+        int over;  // first key - (Nk - 1): row r is clamped when r + over > 0
     };
     auto plan_step = [&](const Step &s, u32x4 *dst) __attribute__((always_inline)) {
         DmaPlan d;
@@ -356,7 +364,7 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         d.vdst = d.kdst + G::CH * 16;
         d.kb = Kb + (int64_t)s.key0 * rs2;
         d.vb = Vb + (int64_t)s.key0 * rs2;
-        d.over = s.key0 - (N - 1);
+        d.over = s.key0 - (Nk - 1);
         return d;
     };
     auto issue_dma = [&](const DmaPlan &d, int i) __attribute__((always_inline)) {
@@ -405,7 +413,15 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     const int32_t *list_a = LIST ? p.skiplist + row_a * (1 + Tk) : nullptr;
     const int32_t *list_b = (LIST && has_b) ? p.skiplist + (row_a + 1) * (1 + Tk) : nullptr;
     LivePair<LIST> it;
-    it.init(mrow_a, list_a, mrow_b, list_b, Tk, has_b);
+    // this lane's words (lane, lane + 64) of the per-tile range bits
+    uint32_t rdo[2] = {0u, 0u}, rsk[2] = {0u, 0u};
+    if (ranges && !LIST) {
+        rdo[0] = p.rg.do_bits[lane];
+        rdo[1] = p.rg.do_bits[lane + 64];
+        rsk[0] = p.rg.skip_bits[lane];
+        rsk[1] = p.rg.skip_bits[lane + 64];
+    }
+    it.init(mrow_a, list_a, mrow_b, list_b, Tk, has_b, rdo, rsk);
     int g_fl = 0;
     int g_kt = it.next(g_fl, Tk);
     int g_sub = 0;
@@ -422,8 +438,8 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         return s;
     };
     auto mine = [&](const Step &s) __attribute__((always_inline)) { return s.kt >= 0 && ((s.fl >> half) & 1); };
-    auto act = [&](const Step &s) __attribute__((always_inline)) { return mine(s) && s.key0 < N; };
-    auto loadable = [&](const Step &s) __attribute__((always_inline)) { return s.kt >= 0 && s.key0 < N; };
+    auto act = [&](const Step &s) __attribute__((always_inline)) { return mine(s) && s.key0 < Nk; };
+    auto loadable = [&](const Step &s) __attribute__((always_inline)) { return s.kt >= 0 && s.key0 < Nk; };
 
     // ---- O^T += V^T P^T over one step (V in LDS stage vst) ----
     // MFMA order ks-major over the D/32 independent accumulators; two
@@ -505,12 +521,12 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         }
         if (act(s)) {
             // keys past the end of the sequence do not exist
-            if (s.key0 + HK > N) {
+            if (s.key0 + HK > Nk) {
 #pragma unroll
                 for (int kb = 0; kb < HK / 32; ++kb)
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
-                        if (s.key0 + kb * 32 + 16 * (v >> 3) + 8 * g + (v & 7) >= N)
+                        if (s.key0 + kb * 32 + 16 * (v >> 3) + 8 * g + (v & 7) >= Nk)
                             S[kb][v] = -INFINITY;
             }
             // step-local max (log2 units)
@@ -549,7 +565,9 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
             }
         }
         if (vote && mine(s) && s.sub == SPT - 1) {
-            const bool keep_lane = qvalid && !(m_tile - m_before < tau2);
+            // a must-do tile is never marked
+            const bool must_do = ranges && ((p.rg.do_bits[s.kt >> 5] >> (s.kt & 31)) & 1u);
+            const bool keep_lane = must_do || (qvalid && !(m_tile - m_before < tau2));
             if (__ballot(keep_lane) != 0ull && lane == 0)
                 lds_or(&keep[half][s.kt >> 5], 1u << (s.kt & 31));
         }
@@ -636,7 +654,7 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     const float l_tot = l_run + other_half(l_run);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     if (qvalid) {
-        __bf16 *Ob = (__bf16 *)p.out + base + (int64_t)qi * rs;
+        __bf16 *Ob = (__bf16 *)p.out + (int64_t)b * p.o_sb + (int64_t)h * D + (int64_t)qi * rs;
 #pragma unroll
         for (int eb = 0; eb < D / 32; ++eb) {
             bf16x8 lo, hi;
@@ -650,7 +668,7 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
             dst[1] = __builtin_bit_cast(u32x4, hi);
         }
         if (p.lse && g == 0)
-            p.lse[bh * N + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+            p.lse[bh * Nq + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     }
     if (vote) {
         __syncthreads();

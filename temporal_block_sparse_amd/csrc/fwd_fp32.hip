@@ -29,26 +29,30 @@ fwd_fp32_kernel(FwdParams p)
     __shared__ uint32_t keep[MAXW];
 
     const int lane = threadIdx.x;
-    const int N = p.N, H = p.H, Tq = p.Tq, Tk = p.Tk, W = p.W;
+    const int Nq = p.Nq, Nk = p.Nk, H = p.H, Tq = p.Tq, Tk = p.Tk, W = p.W;
     const int64_t row = blockIdx.x;
     const int qt = (int)(row % Tq);
     const int64_t bh = row / Tq;
     const int h = (int)(bh % H), b = (int)(bh / H);
     const int64_t rs = (int64_t)H * DIM;
-    const int64_t base = (int64_t)b * N * rs + (int64_t)h * DIM;
-    const float *Qb = (const float *)p.q + base;
-    const float *Kb = (const float *)p.k + base;
-    const float *Vb = (const float *)p.v + base;
+    const int64_t qbase = (int64_t)b * p.q_sb + (int64_t)h * DIM;
+    const int64_t kvbase = (int64_t)b * p.kv_sb + (int64_t)h * DIM;
+    const float *Qb = (const float *)p.q + qbase;
+    const float *Kb = (const float *)p.k + kvbase;
+    const float *Vb = (const float *)p.v + kvbase;
     const uint32_t *mrow = p.mask_in ? p.mask_in + row * W : nullptr;
     const int32_t *list = p.skiplist ? p.skiplist + row * (1 + Tk) : nullptr;
     const bool vote = p.mask_out != nullptr;
+    const bool ranges = p.rg.any != 0;
     const double scale = p.scale, tau = p.tau;
 
+    // keep-vector: a clear bit marks the tile in mask_out.  Must-skip tiles are
+    // never visited and never marked, so their bits start set.
     for (int w = lane; w < W; w += 64)
-        keep[w] = 0u;
+        keep[w] = ranges ? p.rg.skip_bits[w] : 0u;
 
     const int qi = qt * TILE + lane;
-    const bool qvalid = qi < N;
+    const bool qvalid = qi < Nq;
     float qv[DIM];
 #pragma unroll
     for (int e = 0; e < DIM; ++e)
@@ -61,15 +65,22 @@ fwd_fp32_kernel(FwdParams p)
     double m_run = -INFINITY, l_run = 0.0;
 
     // live k-tiles in visiting order (descending): Skip-List or mask words
+    // (must-do tiles live whatever the mask says, must-skip tiles never)
+    auto live_word = [&](int w) -> uint32_t {
+        uint32_t bits = mrow ? ~mrow[w] : 0xffffffffu;
+        if (ranges)
+            bits = (bits & ~p.rg.skip_bits[w]) | p.rg.do_bits[w];
+        if (w == W - 1 && (Tk & 31))
+            bits &= (1u << (Tk & 31)) - 1u;
+        return bits;
+    };
     int cnt = 0, idx = 0, wi = W - 1;
     uint32_t cur = 0;
     if (list) {
         cnt = list[0];
         cnt = cnt < 0 ? 0 : (cnt > Tk ? Tk : cnt);
-    } else {
-        cur = mrow ? ~mrow[wi] : 0xffffffffu;
-        if (Tk & 31)
-            cur &= (1u << (Tk & 31)) - 1u;
+    } else if (W > 0) {
+        cur = live_word(wi);
     }
 
     for (;;) {
@@ -83,7 +94,7 @@ fwd_fp32_kernel(FwdParams p)
         } else {
             while (cur == 0 && wi > 0) {
                 --wi;
-                cur = mrow ? ~mrow[wi] : 0xffffffffu;
+                cur = live_word(wi);
             }
             if (cur != 0) {
                 const int bit = 31 - __builtin_clz(cur);
@@ -98,8 +109,8 @@ fwd_fp32_kernel(FwdParams p)
         __syncthreads();  // previous tile fully consumed
         for (int c = 0; c < TILE; ++c) {
             const int key = key0 + c;
-            Ks[c][lane] = key < N ? Kb[(int64_t)key * rs + lane] : 0.f;
-            Vs[c][lane] = key < N ? Vb[(int64_t)key * rs + lane] : 0.f;
+            Ks[c][lane] = key < Nk ? Kb[(int64_t)key * rs + lane] : 0.f;
+            Vs[c][lane] = key < Nk ? Vb[(int64_t)key * rs + lane] : 0.f;
         }
         __syncthreads();
 
@@ -111,11 +122,13 @@ fwd_fp32_kernel(FwdParams p)
 #pragma unroll
             for (int e = 0; e < DIM; ++e)
                 dot = fma((double)qv[e], (double)Ks[c][e], dot);
-            s[c] = (key0 + c < N) ? dot * scale : -INFINITY;
+            s[c] = (key0 + c < Nk) ? dot * scale : -INFINITY;
             mloc = fmax(mloc, s[c]);
         }
         if (vote) {
-            const bool keep_lane = qvalid && !(mloc - m_run < tau);
+            // a must-do tile is never marked
+            const bool must_do = ranges && ((p.rg.do_bits[kt >> 5] >> (kt & 31)) & 1u);
+            const bool keep_lane = must_do || (qvalid && !(mloc - m_run < tau));
             if (__ballot(keep_lane) != 0ull && lane == 0)
                 atomicOr(&keep[kt >> 5], 1u << (kt & 31));
         }
@@ -137,13 +150,13 @@ fwd_fp32_kernel(FwdParams p)
     }
 
     if (qvalid) {
-        float *Ob = (float *)p.out + base + (int64_t)qi * rs;
+        float *Ob = (float *)p.out + (int64_t)b * p.o_sb + (int64_t)h * DIM + (int64_t)qi * rs;
         const double inv = l_run > 0.0 ? 1.0 / l_run : 0.0;
 #pragma unroll
         for (int e = 0; e < DIM; ++e)
             Ob[e] = (float)(o[e] * inv);
         if (p.lse)
-            p.lse[bh * N + qi] = l_run > 0.0 ? (float)(m_run + log(l_run)) : -INFINITY;
+            p.lse[bh * Nq + qi] = l_run > 0.0 ? (float)(m_run + log(l_run)) : -INFINITY;
     }
     if (vote) {
         __syncthreads();

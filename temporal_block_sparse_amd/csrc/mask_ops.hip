@@ -5,7 +5,9 @@
 // Skip-List is its compacted form for high sparsity (skill page "Lite
 // Attention Temporal Sparse", "Architecture Overview": bitmask, or Skip-List
 // for high sparsity): per row, the count of live k-tiles followed by the live
-// k-tiles in the order the forward visits them (descending).
+// k-tiles in the order the forward visits them (descending).  With token
+// ranges (README Python API: must_do_list / must_skip_list) a must-do tile is
+// live whatever the mask says and a must-skip tile never is.
 #include "lite_attn_internal.h"
 
 namespace lite_attn {
@@ -25,7 +27,8 @@ __global__ void __launch_bounds__(256) reset_kernel(uint32_t *mask, int64_t word
 // lane i looks at tile base - i, a ballot finds the live ones, and each live
 // lane's slot is the number of live lanes below it, so the list comes out in
 // descending order with no sort.
-__global__ void __launch_bounds__(256) skiplist_kernel(const uint32_t *mask, int32_t *list, int64_t rows, int Tk)
+__global__ void __launch_bounds__(256) skiplist_kernel(const uint32_t *mask, int32_t *list, int64_t rows, int Tk,
+                                                       TileRanges rg)
 {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -40,6 +43,12 @@ __global__ void __launch_bounds__(256) skiplist_kernel(const uint32_t *mask, int
         bool live = kt >= 0;
         if (live && mrow)
             live = ((mrow[kt >> 5] >> (kt & 31)) & 1u) == 0u;
+        if (kt >= 0 && rg.any) {
+            if ((rg.do_bits[kt >> 5] >> (kt & 31)) & 1u)
+                live = true;
+            else if ((rg.skip_bits[kt >> 5] >> (kt & 31)) & 1u)
+                live = false;
+        }
         const unsigned long long bal = __ballot(live);
         const int below = __popcll(bal & ((1ull << lane) - 1ull));
         if (live)
@@ -64,12 +73,12 @@ hipError_t launch_reset_mask(uint32_t *mask, int64_t words, hipStream_t stream)
 }
 
 hipError_t launch_build_skiplist(const uint32_t *mask, int32_t *skiplist, int64_t rows, int32_t Tk,
-                                 hipStream_t stream)
+                                 const TileRanges &rg, hipStream_t stream)
 {
     if (rows <= 0)
         return hipSuccess;
     const int64_t blocks = (rows + 3) / 4;
-    hipLaunchKernelGGL(skiplist_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, mask, skiplist, rows, Tk);
+    hipLaunchKernelGGL(skiplist_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, mask, skiplist, rows, Tk, rg);
     return hipGetLastError();
 }
 

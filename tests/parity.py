@@ -29,13 +29,14 @@ def words_to_u32(m):
 
 
 def gpu_fwd(q, k, v, BM, BN, tau, scale, mask_in=None, mark=True, use_skiplist=False, inplace=False,
-            want_lse=True):
-    """Run the HIP forward on device copies of q, k, v (any device).  mask_in:
-    host or device words or None.  Returns (out, lse, mask_out) on the CPU
-    (mask_out None when mark is False)."""
+            want_lse=True, must_do=None, must_skip=None):
+    """Run the HIP forward on device copies of q [B,Nq,H,D] and k, v [B,Nk,H,D]
+    (any device).  mask_in: host or device words or None.  must_do/must_skip:
+    key ranges.  Returns (out, lse, mask_out) on the CPU (mask_out None when
+    mark is False)."""
     dev = torch.device("cuda")
     qd, kd, vd = (t.to(dev).contiguous() for t in (q, k, v))
-    desc = la.desc_of(qd, BM, BN)
+    desc = la.desc_of(qd, BM, BN, kd)
     nw = la.lite_attn_mask_words(desc)
     mi = None
     if mask_in is not None:
@@ -53,18 +54,18 @@ def gpu_fwd(q, k, v, BM, BN, tau, scale, mask_in=None, mark=True, use_skiplist=F
     sl = None
     if use_skiplist:
         sl = torch.full((la.lite_attn_skiplist_len(desc),), -7, dtype=torch.int32, device=dev)
-        la.lite_attn_build_skiplist(desc, mi, sl)
+        la.lite_attn_build_skiplist(desc, mi, sl, must_do, must_skip)
     out = torch.full_like(qd, float("nan"))
     lse = torch.full((qd.shape[0], qd.shape[2], qd.shape[1]), float("nan"), device=dev) if want_lse else None
     la.lite_attn_fwd(qd, kd, vd, out, tile_m=BM, tile_n=BN, tau=tau, softmax_scale=scale, mask_in=mi,
-                     mask_out=mo, skiplist=sl, lse=lse)
+                     mask_out=mo, skiplist=sl, lse=lse, must_do=must_do, must_skip=must_skip)
     torch.cuda.synchronize()
     return (out.cpu(), lse.cpu() if lse is not None else None,
             mo.cpu().numpy().view(np.uint32).reshape(-1, desc_words(desc)) if mo is not None else None)
 
 
 def desc_words(desc):
-    tk = -(-desc.seqlen // desc.tile_n)
+    tk = -(-desc.seqlen_kv // desc.tile_n)
     return -(-tk // 32)
 
 
@@ -72,11 +73,12 @@ def row_coords(row, H, Tq):
     return int(row // (Tq * H)), int((row // Tq) % H), int(row % Tq)
 
 
-def compare_rows(gpu, orc, rows, B, N, H, BM, BN, tau, dtype, mask_checked=True):
-    """Compare GPU results (full tensors) with packed oracle rows.  Returns a
-    dict of error statistics; raises AssertionError on a violation."""
+def compare_rows(gpu, orc, rows, B, N, H, BM, BN, tau, dtype, mask_checked=True, Nk=None):
+    """Compare GPU results (full tensors) with packed oracle rows; N queries,
+    Nk keys (default N).  Returns a dict of error statistics; raises
+    AssertionError on a violation."""
     out_g, lse_g, mask_g = gpu
-    Tq, Tk = -(-N // BM), -(-N // BN)
+    Tq, Tk = -(-N // BM), -(-(N if Nk is None else Nk) // BN)
     W = -(-Tk // 32)
     og = out_g.to(torch.float64).numpy()
     lg = lse_g.numpy().astype(np.float64) if lse_g is not None else None
@@ -117,12 +119,15 @@ def compare_rows(gpu, orc, rows, B, N, H, BM, BN, tau, dtype, mask_checked=True)
     return stats
 
 
-def check_full(q, k, v, BM, BN, tau, scale, mask_in=None, use_skiplist=False, nthreads=None):
+def check_full(q, k, v, BM, BN, tau, scale, mask_in=None, use_skiplist=False, nthreads=None, must_do=None,
+               must_skip=None):
     """All rows: GPU vs oracle.  Returns (stats, oracle result)."""
     B, N, H, D = q.shape
-    orc = oracle.fwd(q, k, v, BM, BN, tau, scale, mask_in=mask_in, nthreads=nthreads)
-    gpu = gpu_fwd(q, k, v, BM, BN, tau, scale, mask_in=mask_in, use_skiplist=use_skiplist)
-    stats = compare_rows(gpu, orc, orc["rows"], B, N, H, BM, BN, tau, q.dtype)
+    orc = oracle.fwd(q, k, v, BM, BN, tau, scale, mask_in=mask_in, nthreads=nthreads, must_do=must_do,
+                     must_skip=must_skip)
+    gpu = gpu_fwd(q, k, v, BM, BN, tau, scale, mask_in=mask_in, use_skiplist=use_skiplist, must_do=must_do,
+                  must_skip=must_skip)
+    stats = compare_rows(gpu, orc, orc["rows"], B, N, H, BM, BN, tau, q.dtype, Nk=k.shape[1])
     return stats, orc
 
 

@@ -27,14 +27,25 @@ def declared_functions():
 def desc(**kw):
     d = dict(BF16)
     d.update(kw)
-    return la.Desc(d["batch"], d["seqlen"], d["heads"], d["head_dim"], d["tile_m"], d["tile_n"], d["dtype"])
+    return la.Desc(d["batch"], d["seqlen"], d["heads"], d["head_dim"], d["tile_m"], d["tile_n"], d["dtype"],
+                   d.get("seqlen_kv", d["seqlen"]), d.get("q_batch_stride", 0), d.get("kv_batch_stride", 0),
+                   d.get("out_batch_stride", 0))
 
 
 def fwd(d, q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), mask_in=None, mask_out=None, skiplist=None,
-        tau=-3.0, scale=0.125, out=FAKE + (3 << 30), lse=None):
+        tau=-3.0, scale=0.125, out=FAKE + (3 << 30), lse=None, ranges=None):
     P = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
     return la.LIB.lite_attn_fwd(ctypes.byref(d) if d is not None else None, P(q), P(k), P(v), P(mask_in),
-                                P(mask_out), P(skiplist), tau, scale, P(out), P(lse), None)
+                                P(mask_out), P(skiplist), tau, scale, P(out), P(lse),
+                                ctypes.byref(ranges) if ranges is not None else None, None)
+
+
+def merge(d, outs, lses, out, lse=None):
+    n = len(outs)
+    po = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(x) if x else None for x in outs])
+    pl = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(x) if x else None for x in lses])
+    return la.LIB.lite_attn_merge(ctypes.byref(d), n, po, pl, ctypes.c_void_p(out) if out else None,
+                                  ctypes.c_void_p(lse) if lse else None, None)
 
 
 def test_every_declared_symbol_is_exported():
@@ -43,7 +54,7 @@ def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(la.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert la.LIB.lite_attn_abi_version() == 1
+    assert la.LIB.lite_attn_abi_version() == 2
 
 
 def test_sizes():
@@ -58,7 +69,7 @@ def test_sizes():
 
 
 def test_strerror_covers_every_code():
-    for code in range(0, 9):
+    for code in range(0, 10):
         assert la.lite_attn_strerror(code)
     assert "unknown" in la.lite_attn_strerror(1234)
 
@@ -77,7 +88,7 @@ def test_null_arguments():
     assert fwd(None) == 1
     assert fwd(desc(), q=None) == 1
     assert fwd(desc(), out=None) == 1
-    assert la.LIB.lite_attn_build_skiplist(ctypes.byref(desc()), None, None, None) == 1
+    assert la.LIB.lite_attn_build_skiplist(ctypes.byref(desc()), None, None, None, None) == 1
     assert la.LIB.lite_attn_reset_mask(ctypes.byref(desc()), None, None) == 1
 
 
@@ -119,7 +130,7 @@ def test_empty_descriptor_is_a_noop():
     for kw in (dict(seqlen=0), dict(batch=0), dict(heads=0)):
         assert fwd(desc(**kw), q=None, k=None, v=None, out=None) == 0
         assert la.LIB.lite_attn_reset_mask(ctypes.byref(desc(**kw)), None, None) == 0
-        assert la.LIB.lite_attn_build_skiplist(ctypes.byref(desc(**kw)), None, None, None) == 0
+        assert la.LIB.lite_attn_build_skiplist(ctypes.byref(desc(**kw)), None, None, None, None) == 0
     # an empty call still rejects a bad threshold or scale
     assert fwd(desc(seqlen=0), tau=float("nan")) == 4
 
@@ -127,8 +138,8 @@ def test_empty_descriptor_is_a_noop():
 def test_skiplist_and_reset_validation():
     d = desc()
     m = FAKE
-    assert la.LIB.lite_attn_build_skiplist(ctypes.byref(d), ctypes.c_void_p(m), ctypes.c_void_p(m + 2), None) == 6
-    assert la.LIB.lite_attn_build_skiplist(ctypes.byref(d), ctypes.c_void_p(m), ctypes.c_void_p(m + 8), None) == 7
+    assert la.LIB.lite_attn_build_skiplist(ctypes.byref(d), ctypes.c_void_p(m), ctypes.c_void_p(m + 2), None, None) == 6
+    assert la.LIB.lite_attn_build_skiplist(ctypes.byref(d), ctypes.c_void_p(m), ctypes.c_void_p(m + 8), None, None) == 7
     assert la.LIB.lite_attn_reset_mask(ctypes.byref(d), ctypes.c_void_p(m + 1), None) == 6
     assert la.LIB.lite_attn_reset_mask(ctypes.byref(desc(tile_m=-3)), ctypes.c_void_p(m), None) == 2
 
@@ -137,3 +148,92 @@ def test_binding_raises_with_code():
     with pytest.raises(la.LiteAttnError) as ei:
         la._check(3)
     assert ei.value.code == 3
+
+
+def test_sizes_with_separate_key_length():
+    d = desc(seqlen=300, seqlen_kv=1000)          # Tq = 3, Tk = 8
+    assert la.lite_attn_mask_words(d) == 2 * 3 * 1
+    assert la.lite_attn_skiplist_len(d) == 2 * 3 * 9
+    d = desc(seqlen=300, seqlen_kv=0)             # no keys: Tk = 0
+    assert la.lite_attn_mask_words(d) == 0 and la.lite_attn_skiplist_len(d) == 2 * 3
+    assert la.lite_attn_mask_words(desc(seqlen_kv=-1)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_batch_stride=-1), 2), (dict(kv_batch_stride=-8), 2),
+    (dict(batch=2, q_batch_stride=1000 * 2 * 128 - 8), 2),     # batch entries would overlap
+    (dict(batch=2, kv_batch_stride=100), 2),
+    (dict(batch=2, out_batch_stride=1000 * 2 * 128 - 1), 2), (dict(out_batch_stride=-1), 2),
+    (dict(batch=2, out_batch_stride=1000 * 2 * 128 + 2), 6),
+    (dict(batch=2, q_batch_stride=1000 * 2 * 128 + 4), 6),     # 8-byte stride: entries misaligned
+    (dict(batch=2, kv_batch_stride=1000 * 2 * 128 + 8), 0),    # 16-byte multiple: accepted, then ...
+])
+def test_batch_strides(kw, code):
+    if code == 0:
+        assert fwd(desc(**kw), q=None) == 1                   # ... the NULL q is reported
+    else:
+        assert fwd(desc(**kw)) == code
+
+
+def test_strided_extents_are_checked_for_aliasing():
+    d = desc(batch=2, q_batch_stride=4 * 1000 * 2 * 128)
+    # q spans (1 * 4 + 1) * 256000 elements * 2 bytes = 2.56 MB from its start, so buffers starting 1 MB
+    # and 2.5 MB in overlap it (the second lies in the gap-free extent of the second batch entry)
+    assert fwd(d, out=FAKE + (1 << 20)) == 7
+    assert fwd(d, lse=FAKE + 2500000) == 7
+
+
+def _ranges(do=(), skip=()):
+    a = (ctypes.c_int32 * max(len(do), 1))(*do)
+    b = (ctypes.c_int32 * max(len(skip), 1))(*skip)
+    r = la.Ranges(ctypes.cast(a, ctypes.POINTER(ctypes.c_int32)), len(do) // 2,
+                  ctypes.cast(b, ctypes.POINTER(ctypes.c_int32)), len(skip) // 2)
+    r._keep = (a, b)
+    return r
+
+
+@pytest.mark.parametrize("do,skip,code", [
+    ((80, 60, 45, 40, 12, 2), (), 0),       # the README's must_do example
+    ((), (80, 40), 0),                      # the README's must_skip example
+    ((10, -1), (), 0),                      # end -1: the range reaches token 0
+    ((60, 80), (), 9),                      # start must exceed end
+    ((80, 60, 70, 65), (), 9),              # pairs must descend
+    ((80, 60, 60, 50), (), 9),              # ... strictly: end_0 > start_1
+    ((10, -2), (), 9),                      # end below -1
+    ((5, 5), (), 9),
+])
+def test_range_validation(do, skip, code):
+    r = _ranges(do, skip)
+    if code == 0:
+        assert fwd(desc(), ranges=r, q=None) == 1
+    else:
+        assert fwd(desc(), ranges=r) == code
+        assert la.LIB.lite_attn_build_skiplist(ctypes.byref(desc()), None, ctypes.c_void_p(FAKE), ctypes.byref(r),
+                                               None) == code
+
+
+def test_range_list_with_null_pointer():
+    r = la.Ranges(None, 1, None, 0)
+    assert fwd(desc(), ranges=r) == 9
+    r = la.Ranges(None, 0, None, 0)                     # no ranges at all is fine
+    assert fwd(desc(), ranges=r, q=None) == 1
+
+
+def test_merge_validation():
+    d = desc()
+    o = [FAKE, FAKE + (1 << 30)]
+    l = [FAKE + (2 << 30), FAKE + (2 << 30) + (1 << 20)]
+    out, lse = FAKE + (3 << 30), FAKE + (4 << 30)
+    assert merge(d, o, l, None) == 1
+    assert merge(d, [FAKE, 0], l, out) == 1
+    assert merge(d, [], [], out) == 3
+    assert merge(d, o * 5, l * 5, out) == 3                          # more than 8 parts
+    assert merge(desc(head_dim=24), o, l, out) == 3                  # head_dim / 8 not a power of two
+    assert merge(desc(head_dim=1024), o, l, out) == 3
+    assert merge(d, [FAKE + 8, o[1]], l, out) == 6
+    assert merge(d, o, [l[0] + 2, l[1]], out) == 6
+    assert merge(d, o, l, out + 2) == 6
+    assert merge(d, o, l, FAKE + 4096) == 7                          # out partly overlaps a part
+    assert merge(d, o, l, out, lse=l[0] + 4) == 7                    # lse partly overlaps a part's lse
+    assert merge(d, o, l, out, lse=out + 64) == 7                    # lse inside out
+    assert merge(desc(batch=0), o, l, out) == 0                      # empty: no-op
