@@ -214,6 +214,20 @@ int lite_attn_reset_mask(const lite_attn_desc *desc, uint32_t *mask, void *strea
 int lite_attn_merge(const lite_attn_desc *desc, int32_t nparts, const void *const *outs,
                     const float *const *lses, void *out, float *lse, void *stream);
 
+/*
+ * lite_attn_error_sums -- the two sums behind the relative output error used
+ * by the per-timestep threshold calibration ([README] "Error Calibration":
+ * error budgets assigned per timestep, stricter early):
+ *     sums[0] = sum over all elements of (a - b)^2,   sums[1] = sum of b^2,
+ * accumulated in fp64 (order unspecified), so ||a - b|| / ||b|| =
+ * sqrt(sums[0] / sums[1]).
+ *   desc      batch, seqlen, heads, head_dim (a multiple of 8) and dtype; a is
+ *             laid out with q_batch_stride, b with out_batch_stride.
+ *   a, b      device, 16-byte aligned; read only.
+ *   sums      device, 2 doubles, 8-byte aligned; overwritten (not added to).
+ */
+int lite_attn_error_sums(const lite_attn_desc *desc, const void *a, const void *b, double *sums, void *stream);
+
 /* Text of a return code.  For LITE_ERR_HIP it includes the HIP error text of
  * this thread's last failing call.  Never NULL. */
 const char *lite_attn_strerror(int code);

@@ -11,6 +11,7 @@ Pages: [README] = the LiteAttention project README (moonmath-ai/LiteAttention);
 """
 
 import ctypes
+import math
 import os
 import subprocess
 import numpy as np
@@ -236,4 +237,51 @@ def error_budgets(num_steps, early_step_ratio=0.3):
     out = []
     for t in range(num_steps):
         out.append(0.5 + 0.5 * (t / n_early) if t < n_early else 1.0)
+    return out
+
+
+def calibrate(steps, tile_m, tile_n, scale, base_error, taus, early_step_ratio=0.3, nthreads=None):
+    """Per-timestep thresholds from per-step output-error budgets ([README]
+    "Error Calibration" / "Accumulated-Error Calibration": variable error
+    budgets per timestep, stricter early), on given inputs.
+
+    steps: list of (q, k, v) per denoising step.  taus: candidate thresholds.
+    The budget of step t is base_error * error_budgets(T)[t].  At step t, with
+    the mask M_t carried from the steps before (empty at step 0), a candidate
+    tau gives the marks M' = mask_out(M_t, tau); its error is
+        || attention(M') - attention(nothing skipped) ||_F / || attention(nothing skipped) ||_F
+    over the whole step's output -- the deviation, accumulated over all
+    earlier steps' marks, that the step would carry once the new marks take
+    effect.  The step takes the largest candidate whose error is within its
+    budget (-inf, which marks nothing new, when none is), and carries M'.
+    Returns a list of dicts (tau, error, budget, sparsity, mask) per step.
+    """
+    T = len(steps)
+    mult = error_budgets(T, early_step_ratio)
+    cands = sorted(set(float(t) for t in taus), reverse=True)
+    if -math.inf not in cands:
+        cands.append(-math.inf)
+    mask = None
+    out = []
+    for t, (q, k, v) in enumerate(steps):
+        B, N, H, _ = np.asarray(q.shape)
+        dense = fwd(q, k, v, tile_m, tile_n, -math.inf, scale, nthreads=nthreads)
+        od, _ = unpack_rows(dense, B, N, H, tile_m)
+        norm = float(np.sqrt((od * od).sum()))
+        budget = base_error * mult[t]
+        pick = None
+        for tau in cands:
+            r = fwd(q, k, v, tile_m, tile_n, tau, scale, mask_in=mask, nthreads=nthreads)
+            m2 = r["mask_out"]
+            r2 = fwd(q, k, v, tile_m, tile_n, -math.inf, scale, mask_in=m2, want_mask_out=False, nthreads=nthreads)
+            o2, _ = unpack_rows(r2, B, N, H, tile_m)
+            err = float(np.sqrt(((o2 - od) ** 2).sum())) / norm if norm > 0 else 0.0
+            if err <= budget or tau == -math.inf:   # -inf (nothing new marked) when no candidate fits
+                pick = (tau, err, m2)
+                break
+        tau, err, m2 = pick
+        tk = -(-k.shape[1] // tile_n)
+        bits = np.unpackbits(m2.view(np.uint8), bitorder="little").reshape(m2.shape[0], -1)[:, :tk]
+        out.append({"tau": tau, "error": err, "budget": budget, "sparsity": float(bits.mean()), "mask": m2})
+        mask = m2
     return out

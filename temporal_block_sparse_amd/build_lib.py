@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblite_attn.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["lite_attn_api.cpp", "fwd_bf16.hip", "fwd_fp32.hip", "mask_ops.hip", "merge.hip"]
+SOURCES = ["lite_attn_api.cpp", "fwd_bf16.hip", "fwd_fp32.hip", "mask_ops.hip", "merge.hip", "calib_ops.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for all device code.

@@ -397,4 +397,40 @@ int lite_attn_merge(const lite_attn_desc *desc, int32_t nparts, const void *cons
     return e == hipSuccess ? LITE_OK : hip_fail(e);
 }
 
+int lite_attn_error_sums(const lite_attn_desc *desc, const void *a, const void *b, double *sums, void *stream)
+{
+    Dims r;
+    int rc = check_desc(desc, &r);
+    if (rc != LITE_OK)
+        return rc;
+    if ((desc->dtype != LITE_BF16 && desc->dtype != LITE_FP32) || desc->head_dim % 8 != 0)
+        return LITE_ERR_UNSUPPORTED;
+    if (!sums)
+        return LITE_ERR_NULL_ARG;
+    if (!aligned(sums, 8))
+        return LITE_ERR_MISALIGNED;
+    if (!empty(desc)) {
+        if (!a || !b)
+            return LITE_ERR_NULL_ARG;
+        if (!aligned(a, 16) || !aligned(b, 16) || !strides_aligned(desc, r))
+            return LITE_ERR_MISALIGNED;
+        const size_t es = elem_size(desc->dtype);
+        if (overlap(sums, 16, a, (size_t)r.q_extent * es) || overlap(sums, 16, b, (size_t)r.o_extent * es))
+            return LITE_ERR_ALIAS;
+    }
+    lite_attn::ErrParams p;
+    p.a = a;
+    p.b = b;
+    p.sums = sums;
+    p.B = desc->batch;
+    p.N = desc->seqlen;
+    p.H = desc->heads;
+    p.D = desc->head_dim;
+    p.dtype = desc->dtype;
+    p.a_sb = r.q_sb;
+    p.b_sb = r.o_sb;
+    const hipError_t e = lite_attn::launch_error_sums(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LITE_OK : hip_fail(e);
+}
+
 }  // extern "C"

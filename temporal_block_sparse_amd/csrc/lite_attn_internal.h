@@ -44,11 +44,19 @@ struct MergeParams {
     int64_t q_sb, o_sb;        // batch strides of the parts and of out
 };
 
+struct ErrParams {
+    const void *a, *b;
+    double *sums;
+    int32_t B, N, H, D, dtype;
+    int64_t a_sb, b_sb;        // batch strides of a and b
+};
+
 hipError_t launch_fwd_bf16(const FwdParams &p, hipStream_t stream);
 hipError_t launch_fwd_fp32(const FwdParams &p, hipStream_t stream);
 hipError_t launch_build_skiplist(const uint32_t *mask, int32_t *skiplist, int64_t rows, int32_t Tk,
                                  const TileRanges &rg, hipStream_t stream);
 hipError_t launch_reset_mask(uint32_t *mask, int64_t words, hipStream_t stream);
 hipError_t launch_merge(const MergeParams &p, hipStream_t stream);
+hipError_t launch_error_sums(const ErrParams &p, hipStream_t stream);
 
 }  // namespace lite_attn

@@ -28,7 +28,8 @@ ERRORS = {1: "LITE_ERR_NULL_ARG", 2: "LITE_ERR_BAD_SHAPE", 3: "LITE_ERR_UNSUPPOR
           5: "LITE_ERR_BAD_SCALE", 6: "LITE_ERR_MISALIGNED", 7: "LITE_ERR_ALIAS", 8: "LITE_ERR_HIP",
           9: "LITE_ERR_BAD_RANGES"}
 EXPORTS = ("lite_attn_fwd", "lite_attn_build_skiplist", "lite_attn_reset_mask", "lite_attn_merge",
-           "lite_attn_mask_words", "lite_attn_skiplist_len", "lite_attn_strerror", "lite_attn_abi_version")
+           "lite_attn_error_sums", "lite_attn_mask_words", "lite_attn_skiplist_len", "lite_attn_strerror",
+           "lite_attn_abi_version")
 
 
 class Desc(ctypes.Structure):
@@ -65,6 +66,8 @@ def _load():
     lib.lite_attn_reset_mask.argtypes = [D, P, P]
     lib.lite_attn_merge.restype = ctypes.c_int
     lib.lite_attn_merge.argtypes = [D, ctypes.c_int32, ctypes.POINTER(P), ctypes.POINTER(P), P, P, P]
+    lib.lite_attn_error_sums.restype = ctypes.c_int
+    lib.lite_attn_error_sums.argtypes = [D, P, P, P, P]
     lib.lite_attn_mask_words.restype = ctypes.c_size_t
     lib.lite_attn_mask_words.argtypes = [D]
     lib.lite_attn_skiplist_len.restype = ctypes.c_size_t
@@ -223,6 +226,20 @@ def lite_attn_merge(outs, lses, out, lse=None, stream=None):
     pl = (ctypes.c_void_p * n)(*[_ptr(x) for x in lses])
     _check(LIB.lite_attn_merge(ctypes.byref(desc), n, po, pl, optr, _ptr(lse), _stream(stream)))
     return out
+
+
+def lite_attn_error_sums(a, b, sums=None, stream=None):
+    """C lite_attn_error_sums: (sum (a-b)^2, sum b^2) in fp64 for two BSHD
+    tensors of one shape.  Returns the device tensor of the two sums."""
+    B, N, H, D, as_, ap = _bshd(a)
+    bs = _bshd(b)
+    if b.shape != a.shape or b.dtype != a.dtype:
+        raise ValueError("a and b must share shape and dtype")
+    if sums is None:
+        sums = torch.empty(2, dtype=torch.float64, device=a.device)
+    desc = make_desc(B, N, H, D, 1, 1, a.dtype, N, as_, 0, bs[4])
+    _check(LIB.lite_attn_error_sums(ctypes.byref(desc), ap, bs[5], _ptr(sums), _stream(stream)))
+    return sums
 
 
 def alloc_mask(desc, device="cuda"):

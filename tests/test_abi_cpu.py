@@ -237,3 +237,18 @@ def test_merge_validation():
     assert merge(d, o, l, out, lse=l[0] + 4) == 7                    # lse partly overlaps a part's lse
     assert merge(d, o, l, out, lse=out + 64) == 7                    # lse inside out
     assert merge(desc(batch=0), o, l, out) == 0                      # empty: no-op
+
+
+def test_error_sums_validation():
+    P = ctypes.c_void_p
+    d = desc()
+    a, b, s = P(FAKE), P(FAKE + (1 << 30)), P(FAKE + (2 << 30))
+    f = la.LIB.lite_attn_error_sums
+    assert f(None, a, b, s, None) == 1
+    assert f(ctypes.byref(d), a, b, None, None) == 1
+    assert f(ctypes.byref(d), None, b, s, None) == 1
+    assert f(ctypes.byref(d), a, b, P(FAKE + (2 << 30) + 4), None) == 6
+    assert f(ctypes.byref(d), P(FAKE + 8), b, s, None) == 6
+    assert f(ctypes.byref(desc(head_dim=12)), a, b, s, None) == 3
+    assert f(ctypes.byref(desc(dtype=5)), a, b, s, None) == 3
+    assert f(ctypes.byref(d), a, b, P(FAKE + 4096), None) == 7         # sums inside a

@@ -1,0 +1,99 @@
+"""GPU parity of the per-timestep threshold calibration and of the error sums
+it is built on, against the CPU oracle's calibration (fp64) on the same
+seeded drifting inputs.
+
+The calibration compares a candidate's relative output error with the step's
+budget; bf16 outputs move that error by about 2^-9 relative, so a step whose
+oracle error for the chosen or the next candidate lies within 3e-3 of the
+budget is a tie: from there on either choice is accepted and the trajectories
+are no longer compared."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from temporal_block_sparse_amd import calibrate, configs, synth
+from temporal_block_sparse_amd import lite_attn as la
+
+pytestmark = pytest.mark.gpu
+
+TIE = 3e-3
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_error_sums_match_numpy(dtype):
+    g = torch.Generator().manual_seed(1)
+    full_a = torch.randn(2, 300, 3, 64, generator=g).to(dtype)
+    full_b = torch.randn(2, 300, 3, 64, generator=g).to(dtype)
+    a, b = full_a[:, 17:217], full_b[:, 50:250]                      # strided slices
+    dev = torch.device("cuda")
+    s = la.lite_attn_error_sums(full_a.to(dev)[:, 17:217], full_b.to(dev)[:, 50:250]).cpu().numpy()
+    an, bn = a.double().numpy(), b.double().numpy()
+    ref = np.array([((an - bn) ** 2).sum(), (bn ** 2).sum()])
+    assert np.allclose(s, ref, rtol=1e-12, atol=0)
+    # a second call overwrites, it does not add
+    s2 = la.lite_attn_error_sums(full_a.to(dev)[:, 17:217], full_b.to(dev)[:, 50:250]).cpu().numpy()
+    assert np.allclose(s2, ref, rtol=1e-12, atol=0)
+
+
+def test_budgets_match_the_oracle_schedule():
+    for T, r in ((50, 0.3), (10, 0.5), (3, 0.3), (1, 0.3)):
+        assert calibrate.error_budgets(T, r) == oracle.error_budgets(T, r)
+
+
+@pytest.mark.parametrize("use_skiplist", [False, True])
+def test_calibration_matches_the_oracle(use_skiplist):
+    wl = configs.scaled(configs.C2, (8, 8, 8), heads=2, batch=1, steps=4)     # 512 tokens, d = 64, tile 128x64
+    tr = synth.Trajectory(wl, "cpu")
+    steps = []
+    for t in range(wl.steps):
+        if t:
+            tr.advance()
+        steps.append(tr.tensors())
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    taus = [0.0, -1.0, -2.0, -3.0, -5.0, -8.0]
+    base = 0.03
+    orc = oracle.calibrate(steps, wl.tile_m, wl.tile_n, scale, base, taus)
+    dev = torch.device("cuda")
+    gpu = calibrate.calibrate_thresholds([tuple(x.to(dev) for x in s) for s in steps], wl.tile_m, wl.tile_n, base,
+                                         taus, softmax_scale=scale, use_skiplist=use_skiplist)
+    cands = sorted(taus, reverse=True) + [-math.inf]
+    for t, (o, g) in enumerate(zip(orc, gpu)):
+        log("  step %d oracle tau %g err %.4g budget %.4g | gpu tau %g err %.4g sparsity %.3f"
+            % (t, o["tau"], o["error"], o["budget"], g["tau"], g["error"], g["sparsity"]))
+        assert g["budget"] == o["budget"]
+        if o["tau"] == g["tau"]:
+            assert abs(g["error"] - o["error"]) <= TIE
+            mg = g["mask"].cpu().numpy().view(np.uint32).reshape(o["mask"].shape)
+            if not np.array_equal(mg, o["mask"]):
+                log("  masks differ at step %d (threshold ties): stop comparing" % t)
+                break
+            continue
+        # different choices are only accepted at a tie: re-evaluate the two candidates with the oracle
+        i = cands.index(o["tau"])
+        nxt = cands[i - 1] if i > 0 else None
+        near = abs(o["error"] - o["budget"]) <= TIE
+        if nxt is not None and not near:
+            mask_in = orc[t - 1]["mask"] if t else None
+            q, k, v = steps[t]
+            B, N, H, _ = q.shape
+            dense = oracle.fwd(q, k, v, wl.tile_m, wl.tile_n, -math.inf, scale)
+            od, _ = oracle.unpack_rows(dense, B, N, H, wl.tile_m)
+            m2 = oracle.fwd(q, k, v, wl.tile_m, wl.tile_n, nxt, scale, mask_in=mask_in)["mask_out"]
+            o2, _ = oracle.unpack_rows(oracle.fwd(q, k, v, wl.tile_m, wl.tile_n, -math.inf, scale, mask_in=m2),
+                                       B, N, H, wl.tile_m)
+            err_next = float(np.sqrt(((o2 - od) ** 2).sum() / (od ** 2).sum()))
+            near = abs(err_next - o["budget"]) <= TIE
+        assert near, "step %d: gpu tau %g vs oracle tau %g away from a tie" % (t, g["tau"], o["tau"])
+        log("  tie at step %d: stop comparing" % t)
+        break
+    assert any(g["sparsity"] > 0 for g in gpu)

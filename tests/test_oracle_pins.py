@@ -231,3 +231,59 @@ def test_error_budgets_follow_the_printed_schedule():
     assert b[:15] == sorted(b[:15])
     assert oracle.error_budgets(3, 0.3) == [1.0, 1.0, 1.0]    # int(0.9) = 0 early steps
     assert oracle.error_budgets(10, 0.5)[:5] == [0.5, 0.6, 0.7, 0.8, 0.9]
+
+
+def _calib_inputs(steps=3, N=96, H=2, D=8, seed=0):
+    """A tiny drifting trajectory with a locality bias, so thresholds matter."""
+    g = torch.Generator().manual_seed(seed)
+    pos = torch.arange(N, dtype=torch.float64)
+    feat = torch.stack([torch.cos(pos / 6.0 * (j + 1)) for j in range(D)], -1)    # smooth in the position
+    q0 = 3.0 * feat[None, :, None, :].expand(1, N, H, D) + torch.randn(1, N, H, D, generator=g, dtype=torch.float64)
+    k0 = 3.0 * feat[None, :, None, :].expand(1, N, H, D) + torch.randn(1, N, H, D, generator=g, dtype=torch.float64)
+    v0 = torch.randn(1, N, H, D, generator=g, dtype=torch.float64)
+    out = []
+    for t in range(steps):
+        out.append((q0 + 0.05 * t * torch.randn(1, N, H, D, generator=g, dtype=torch.float64),
+                    k0 + 0.05 * t * torch.randn(1, N, H, D, generator=g, dtype=torch.float64), v0))
+    return out
+
+
+def test_calibration_picks_the_largest_feasible_threshold():
+    """Re-evaluated by brute force at every step: the chosen tau's error is
+    within the budget and every larger candidate's is not (numpy attention over
+    the visited tiles, against numpy dense attention)."""
+    steps = _calib_inputs()
+    BM = BN = 16
+    taus = [0.0, -1.0, -2.0, -3.0, -5.0, -8.0]
+    scale = 0.35
+    res = oracle.calibrate(steps, BM, BN, scale, base_error=0.02, taus=taus)
+    budgets = oracle.error_budgets(len(steps))
+    mask = np.zeros((2 * 6, 1), np.uint32)
+    saw_skip = False
+    for t, ((q, k, v), r) in enumerate(zip(steps, res)):
+        assert r["budget"] == 0.02 * budgets[t]
+        o_dense, _, _ = oc.dense_reference(q, k, v, scale)
+        norm = np.sqrt((o_dense ** 2).sum())
+        for tau in sorted(taus + [-math.inf], reverse=True):
+            m2 = oracle.fwd(q, k, v, BM, BN, tau, scale, mask_in=mask)["mask_out"]
+            o2, _, _ = oc.dense_reference(q, k, v, scale, oc.bits_of(m2, 6), BM, BN)
+            err = np.sqrt(((o2 - o_dense) ** 2).sum()) / norm
+            if tau > r["tau"]:
+                assert err > r["budget"], (t, tau)
+            elif tau == r["tau"]:
+                assert abs(err - r["error"]) < 1e-12
+                assert err <= r["budget"] or tau == -math.inf
+                break
+        saw_skip = saw_skip or r["sparsity"] > 0
+        mask = r["mask"]
+    assert saw_skip
+
+
+def test_calibration_limits():
+    steps = _calib_inputs(steps=2)
+    taus = [0.0, -2.0, -6.0]
+    # an unbounded budget always takes the most aggressive candidate
+    assert [r["tau"] for r in oracle.calibrate(steps, 16, 16, 0.35, math.inf, taus)] == [0.0, 0.0]
+    # a zero budget never lets a new mark change the output
+    for r in oracle.calibrate(steps, 16, 16, 0.35, 0.0, taus):
+        assert r["error"] == 0.0
