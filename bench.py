@@ -73,6 +73,22 @@ def live_flops(mask_words, wl):
     return 4.0 * d * float((live * rows_valid).sum())
 
 
+def pair_occupancy(mask_words, wl):
+    """Share of the walked steps that both q-tiles of a workgroup compute: one
+    workgroup serves q-tiles 2j and 2j+1 of a (batch, head) and walks the union
+    of their live tiles, so this is sum |live| / (2 sum |union|)."""
+    import torch
+    Tq, Tk = wl.tq, wl.tk
+    w = mask_words.view(wl.batch * wl.heads, Tq, wl.mask_words).to(torch.int64) & 0xFFFFFFFF
+    bits = (w[..., None] >> torch.arange(32, device=w.device)) & 1
+    live = (1 - bits.reshape(wl.batch * wl.heads, Tq, -1)[..., :Tk]).to(torch.float64)
+    if Tq % 2:
+        live = torch.cat([live, torch.zeros_like(live[:, :1])], dim=1)
+    a, b = live[:, 0::2], live[:, 1::2]
+    union = torch.maximum(a, b).sum()
+    return float((a.sum() + b.sum()) / (2.0 * union)) if union > 0 else 1.0
+
+
 def read_traffic(src_hash):
     """(bytes per launch, note) from the committed counter summary, or (None, why)."""
     if not os.path.exists(TRAFFIC_FILE):
@@ -232,6 +248,7 @@ def main():
     src_hash = kernel_source_hash()
     traffic, traffic_note = read_traffic(src_hash)
     sparsity = [1.0 - f / dense_flops for f in flops]
+    occupancy = [pair_occupancy(masks[t], wl) for t in range(K)]
 
     # ---- tau sweep over a trajectory (kernel time per step, per threshold) ----
     sweep = None
@@ -257,7 +274,8 @@ def main():
             torch.cuda.synchronize()
             for tau, ev, m_in in pend:
                 f = dense_flops if m_in is None else live_flops(m_in, wl)
-                rec[tau].append((ev[0].elapsed_time(ev[1]), f))
+                occ = 1.0 if m_in is None else pair_occupancy(m_in, wl)
+                rec[tau].append((ev[0].elapsed_time(ev[1]), f, occ))
             if t % 10 == 0:
                 log("[bench] sweep step %d/%d" % (t, args.sweep_steps))
             tr2.advance()
@@ -272,7 +290,8 @@ def main():
             ent = {"tau": None if math.isinf(tau) else tau, "steps": len(tms), "kernel_ms_total": round(sum(tms), 3),
                    "sparsity_first": round(1 - fl[0] / dense_flops, 4), "sparsity_last": round(1 - fl[-1] / dense_flops, 4),
                    "sparsity_mean": round(1 - sum(fl) / (dense_flops * len(fl)), 4),
-                   "tflops_live": round(sum(fl) / (sum(tms) * 1e-3) / 1e12, 1)}
+                   "tflops_live": round(sum(fl) / (sum(tms) * 1e-3) / 1e12, 1),
+                   "pair_occupancy_mean": round(sum(x[2] for x in rec[tau]) / len(tms), 4)}
             if dense_t:
                 ent["speedup_vs_dense"] = round(sum(dense_t) / sum(tms), 3)
                 for a, b, f in zip(tms, dense_t, fl):
@@ -331,6 +350,7 @@ def main():
         "dense_kernel_ms": round(sum(dense_ms) / K, 3), "kernel_ms": round(sum(kern_ms) / K, 3),
         "dense_tflops": round(dense_flops * K / (sum(dense_ms) * 1e-3) / 1e12, 1),
         "sparsity": [round(s, 4) for s in sparsity],
+        "pair_occupancy": [round(o, 4) for o in occupancy],
         "skiplist_build_ms": round(sl_ms, 4) if sl_ms is not None else None,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

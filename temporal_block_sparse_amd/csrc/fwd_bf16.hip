@@ -36,13 +36,19 @@
 // * The online softmax is updated per 64-key step (exact in any grouping);
 //   the QK-Skip test uses the maximum over all steps of the tile against the
 //   running max taken before its first step.
-// * K and V steps go global -> LDS by direct-to-LDS loads
-//   (global_load_lds_dwordx4): no staging registers, no LDS store
-//   instructions.  Three LDS stages (96 KB at head_dim 128): step u's K is
-//   read in the two phases of step u, its V in the two phases of step u + 1,
-//   and step u + 1 is loaded meanwhile.  A's waves issue the loads during
-//   their QK^T MFMAs, after their PV reads, so no LDS read of this kernel ever
-//   waits for a load in flight; the loads complete at the end of the step.
+// * K and V steps go global -> LDS by direct-to-LDS buffer loads
+//   (buffer_load_dwordx4 ... lds): no staging registers, no LDS store
+//   instructions.  Four LDS stages (128 KB at head_dim 128) and a prefetch
+//   distance of two steps: while step u is computed (its K read in both
+//   phases of step u, its V in both phases of step u + 1), step u + 1 is in
+//   flight and A's waves issue step u + 2 among their QK^T MFMAs.  Each
+//   load's source is a buffer resource (base, byte range) built in scalar
+//   registers per 16 or 32 key rows, so addresses cost no vector
+//   instructions, and rows past the end of the sequence read as zeros through
+//   the range check instead of being clamped.  The loads are issued from asm
+//   blocks, which keeps the compiler from making LDS reads of other stages
+//   wait for them; explicit vmcnt waits publish a stage at the barrier that
+//   ends the step before its first use.
 // * K rows sit in LDS with rows 4..7 and 8..11 of every 16 swapped, so the 8
 //   scores a lane holds per 16-key MFMA step are 8 consecutive keys.  V stays
 //   in natural (key x head-dim) layout and the PV A-operand (V^T) is read with
@@ -244,9 +250,42 @@ struct Step {
 
 // One 16-byte direct-to-LDS load: each lane's `src`, into `dst` + 16 * lane
 // (dst is wave-uniform).
-__device__ __forceinline__ void dma16(const char *src, char *dst)
+// The source is a raw buffer resource (base, byte range) plus this lane's byte
+// offset: an offset at or past the range reads zeros, which is how rows past
+// the end of the sequence are handled.  Issued from an asm block: the compiler
+// does not count these loads, so it never delays an LDS read for them; the
+// kernel waits for them explicitly (vmcnt) before the barriers that publish a
+// stage and before it exits.  The leading s_nop covers the wait states an
+// M0 or SGPR write needs before a buffer load reads it.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t off, char *dst)
 {
-    __builtin_amdgcn_global_load_lds((const void *)src, LDS_VOID(dst), 16, 0, 0);
+    const uint32_t l = (uint32_t)(size_t)LDS_VOID(dst);
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(l));
+}
+
+__device__ __forceinline__ const char *uniform_ptr(const char *x)
+{
+    // readfirstlane returns a signed int: widen through uint32_t, or an
+    // address with bit 31 set would be sign-extended into the high word
+    const uint64_t a = (uint64_t)x;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return (const char *)(lo | (hi << 32));
+}
+
+// Raw buffer resource over [base, base + bytes): no stride, no swizzle,
+// 32-bit data format (required for untyped loads).  The values are
+// wave-uniform; readfirstlane makes that visible to the compiler, which must
+// hold the resource in SGPRs.
+__device__ __forceinline__ u32x4 buffer_rsrc(const char *base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000u;
+    return r;
 }
 
 // LDS layout of one 64-key step.  K and V arrive by direct-to-LDS loads
@@ -266,6 +305,7 @@ struct Geo {
     static constexpr int CH = HK * CPR;     // chunks of a K (or V) step
     static constexpr int STAGE = 2 * CH;    // K then V, in chunks
     static constexpr int IPA = CH / 64 / 4; // DMA instructions per A-wave, per tensor
+    static constexpr int RPI = 256 / CPR;   // key rows covered by one instruction round of the 4 A-waves
     static_assert(CH % (64 * 4) == 0, "unsupported step geometry");
 };
 
@@ -288,11 +328,12 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
 {
     using G = Geo<D>;
     constexpr int SPT = BN / HK;  // steps per k-tile
-    // Three distinct LDS objects, one per pipeline stage: the compiler can then
-    // tell a stage being read from the stage being filled by DMA.
+    // Four distinct LDS objects, one per pipeline stage: the compiler can then
+    // tell a stage being read from the stages being filled by DMA.
     __shared__ u32x4 stage0[G::STAGE];
     __shared__ u32x4 stage1[G::STAGE];
     __shared__ u32x4 stage2[G::STAGE];
+    __shared__ u32x4 stage3[G::STAGE];
     __shared__ uint32_t keep[2][MAXW];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -313,8 +354,8 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     const int64_t qbase = (int64_t)b * p.q_sb + (int64_t)h * D;
     const int64_t kvbase = (int64_t)b * p.kv_sb + (int64_t)h * D;
     const __bf16 *Qb = (const __bf16 *)p.q + qbase;
-    const char *Kb = (const char *)((const __bf16 *)p.k + kvbase);
-    const char *Vb = (const char *)((const __bf16 *)p.v + kvbase);
+    const char *Kb = uniform_ptr((const char *)((const __bf16 *)p.k + kvbase));
+    const char *Vb = uniform_ptr((const char *)((const __bf16 *)p.v + kvbase));
     const bool vote = p.mask_out != nullptr;
     const bool ranges = p.rg.any != 0;
 
@@ -337,41 +378,49 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
 
     // Direct-to-LDS slots of the A-waves, which load every step (fixed for the
     // kernel): DMA instruction i of A-wave wq fills LDS chunks
-    // [(i*4 + wq)*64, +64) of the K (and V) step; this lane's chunk comes from
-    // key row kr[i] (K) / vr[i] (V) of the step, at byte offset kgo[i] / vgo[i]
-    // from the step's first key.
-    int kr[G::IPA], kgo[G::IPA], vr[G::IPA], vgo[G::IPA];
-#pragma unroll
-    for (int i = 0; i < G::IPA; ++i) {
-        const int P = (i * 4 + wq) * 64 + lane;
+    // [(i*4 + wq)*64, +64) of the K (and V) step.  This lane's chunk comes from
+    // key row kr0 + i*RPI (K) / vr0 + i*RPI (V) of the step -- the row pattern
+    // of one instruction round repeats every RPI rows, swizzles included -- at
+    // byte kc0 / vc0 within the row.
+    int kr0, kc0, vr0, vc0;
+    {
+        const int P = wq * 64 + lane;
         const int lr = P / G::CPR, pos = P % G::CPR;
-        kr[i] = kperm(lr);
-        kgo[i] = kr[i] * rs2 + (pos ^ k_swz<D>(lr)) * 16;
-        vr[i] = lr;
-        vgo[i] = lr * rs2 + (pos ^ v_swz<D>(lr)) * 16;
+        kr0 = kperm(lr);
+        kc0 = (pos ^ k_swz<D>(lr)) * 16;
+        vr0 = lr;
+        vc0 = (pos ^ v_swz<D>(lr)) * 16;
     }
-    // The loads of one step into one LDS stage.  Rows past the end of the
-    // sequence are clamped to key Nk-1 (their logits are set to -inf before
-    // use), so every address is in bounds.
+    // The loads of one step into one LDS stage.  Instruction i covers key rows
+    // [key0 + i*RPI, +RPI): its buffer starts at row key0 + i*RPI and spans the
+    // rows of that block that exist, so rows past the end of the sequence read
+    // as zeros (their logits are set to -inf before use) and no address leaves
+    // the tensors.  All of it is scalar arithmetic.
+    const uint32_t koff = (uint32_t)(kr0 * rs2 + kc0);
+    const uint32_t voff = (uint32_t)(vr0 * rs2 + vc0);
     struct DmaPlan {
         const char *kb, *vb;
         char *kdst, *vdst;
-        int over;  // first key - (Nk - 1): row r is clamped when r + over > 0
+        int bytes;  // bytes of the step's rows that exist: min(Nk - key0, HK) rows
     };
-    auto plan_step = [&](const Step &s, u32x4 *dst) __attribute__((always_inline)) {
+    auto plan_step = [&](int key0, u32x4 *dst) __attribute__((always_inline)) {
         DmaPlan d;
         d.kdst = (char *)dst + wq * 64 * 16;
         d.vdst = d.kdst + G::CH * 16;
-        d.kb = Kb + (int64_t)s.key0 * rs2;
-        d.vb = Vb + (int64_t)s.key0 * rs2;
-        d.over = s.key0 - (Nk - 1);
+        d.kb = Kb + (int64_t)key0 * rs2;
+        d.vb = Vb + (int64_t)key0 * rs2;
+        d.bytes = min(Nk - key0, HK) * rs2;
         return d;
     };
     auto issue_dma = [&](const DmaPlan &d, int i) __attribute__((always_inline)) {
-        const int ko = kgo[i] - max(kr[i] + d.over, 0) * rs2;
-        const int vo = vgo[i] - max(vr[i] + d.over, 0) * rs2;
-        dma16(d.kb + ko, d.kdst + i * 4 * 64 * 16);
-        dma16(d.vb + vo, d.vdst + i * 4 * 64 * 16);
+        // bytes of instruction i's RPI rows that exist; max(x, 0) as a sign
+        // mask keeps the clamp in scalar instructions
+        int x = d.bytes - i * G::RPI * rs2;
+        x &= ~(x >> 31);
+        const uint32_t bytes = (uint32_t)min(x, G::RPI * rs2);
+        const int64_t blk = (int64_t)i * G::RPI * rs2;
+        dma16(buffer_rsrc(d.kb + blk, bytes), koff, d.kdst + i * 4 * 64 * 16);
+        dma16(buffer_rsrc(d.vb + blk, bytes), voff, d.vdst + i * 4 * 64 * 16);
     };
 
     // This lane's slot as a source of the transposed V read: key row 8g + a of
@@ -426,11 +475,13 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     int g_kt = it.next(g_fl, Tk);
     int g_sub = 0;
     auto gen = [&]() __attribute__((always_inline)) {
+        // wave-uniform by construction; readfirstlane lets the compiler keep
+        // the step (and the load addresses built from it) in scalar registers
         Step s;
-        s.kt = g_kt;
-        s.sub = g_sub;
-        s.fl = g_fl;
-        s.key0 = g_kt * BN + g_sub * HK;
+        s.kt = __builtin_amdgcn_readfirstlane(g_kt);
+        s.sub = __builtin_amdgcn_readfirstlane(g_sub);
+        s.fl = __builtin_amdgcn_readfirstlane(g_fl);
+        s.key0 = s.kt * BN + s.sub * HK;
         if (g_kt >= 0 && ++g_sub == SPT) {
             g_sub = 0;
             g_kt = it.next(g_fl, Tk);
@@ -442,25 +493,32 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     auto loadable = [&](const Step &s) __attribute__((always_inline)) { return s.kt >= 0 && s.key0 < Nk; };
 
     // ---- O^T += V^T P^T over one step (V in LDS stage vst) ----
-    // MFMA order ks-major over the D/32 independent accumulators; two
-    // transposed reads per MFMA, issued AHEAD MFMAs before their use.
+    // MFMA order ks-major over the D/32 independent accumulators; each
+    // transposed V read is issued AHEAD MFMAs before its use.
     auto pv_gemm = [&](const u32x4 *vst) __attribute__((always_inline)) {
         constexpr int NEB = D / 32, NM = NEB * (HK / 16);
         // lane offsets recomputed here, not kept live across the loop
         int vl = vtr_row * G::CPR * 16 + vtr_col, vsg = vtr_seg;
         asm volatile("" : "+v"(vl), "+v"(vsg));
         const char *Vs = (const char *)(vst + G::CH) + vl;
+        // MFMA m = ks*NEB + eb; its operand is read AHEAD MFMAs earlier
+        s16x8 vf[NM];
+        auto rd = [&](int m) __attribute__((always_inline)) {
+            const int ks = m / NEB, eb = m % NEB;
+            const char *va = Vs + 16 * ks * G::CPR * 16 + ((eb ^ vsg) * 64);
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va + 4 * G::CPR * 16));
+            vf[m] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
 #pragma unroll
-        for (int ks = 0; ks < HK / 16; ++ks) {
+        for (int m = 0; m < AHEAD; ++m)
+            rd(m);
 #pragma unroll
-            for (int eb = 0; eb < NEB; ++eb) {
-                const char *va = Vs + 16 * ks * G::CPR * 16 + ((eb ^ vsg) * 64);
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va + 4 * G::CPR * 16));
-                const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                O[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), P[ks], O[eb], 0, 0,
-                                                                0);
-            }
+        for (int m = 0; m < NM; ++m) {
+            if (m + AHEAD < NM)
+                rd(m + AHEAD);
+            O[m % NEB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[m]), P[m / NEB],
+                                                                 O[m % NEB], 0, 0, 0);
         }
         __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * AHEAD, 0);
 #pragma unroll
@@ -488,18 +546,24 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 S[kb][v] = 0.f;
+        // MFMA m = ds*2 + kb; its K fragment is read AHEAD MFMAs earlier
+        u32x4 kf[NM];
+        auto rd = [&](int m) __attribute__((always_inline)) {
+            const int ds = m >> 1, kb = m & 1;
+            kf[m] = kst[kb * 32 * G::CPR + kl + ((2 * ds) ^ kc)];
+        };
 #pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
+        for (int m = 0; m < AHEAD; ++m)
+            rd(m);
 #pragma unroll
-            for (int kb = 0; kb < HK / 32; ++kb) {
-                const u32x4 a = kst[kb * 32 * G::CPR + kl + ((2 * ds) ^ kc)];
-                S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ds], S[kb], 0, 0,
-                                                                0);
-                // one (K, V) pair per four MFMAs: NM = 4 * IPA for both head dims
-                const int m = ds * (HK / 32) + kb;
-                if (WD && (m & 3) == 3)
-                    issue_dma(dma, m >> 2);
-            }
+        for (int m = 0; m < NM; ++m) {
+            if (m + AHEAD < NM)
+                rd(m + AHEAD);
+            S[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[m]), qf[m >> 1],
+                                                               S[m & 1], 0, 0, 0);
+            // one (K, V) pair per four MFMAs: NM = 4 * IPA for both head dims
+            if (WD && (m & 3) == 3)
+                issue_dma(dma, m >> 2);
         }
         __builtin_amdgcn_sched_group_barrier(SG_DS_READ, AHEAD, 0);
 #pragma unroll
@@ -573,67 +637,82 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         }
     };
 
+    // Every A-wave issues exactly 2*IPA loads per step (real, or empty-range
+    // loads that write zeros to a stage nobody reads and touch no memory), so
+    // that "all but the last 2*IPA loads done" means "the step before the last
+    // one has landed".
+    constexpr int VM_KEEP = 2 * G::IPA;
+    constexpr int WAIT_KEEP = (VM_KEEP & 15) | (7 << 4) | (15 << 8) | ((VM_KEEP >> 4) << 14);  // vmcnt only
+    constexpr int WAIT_ALL = (7 << 4) | (15 << 8);  // vmcnt(0) only
+    auto load_step = [&](const Step &s, u32x4 *dst) __attribute__((always_inline)) {
+        if (Nk <= 0)
+            return;  // no key rows at all
+        const DmaPlan d = plan_step(loadable(s) ? s.key0 : Nk, dst);
+#pragma unroll
+        for (int i = 0; i < G::IPA; ++i)
+            issue_dma(d, i);
+    };
+
     Step sp = {-1, 0, 0, 0};  // step u - 1
     Step sc = gen();          // step u
     Step sn = gen();          // step u + 1
-    if (half == 0 && loadable(sc)) {
-        const DmaPlan d0 = plan_step(sc, stage0);
-#pragma unroll
-        for (int i = 0; i < G::IPA; ++i)
-            issue_dma(d0, i);
+    Step sn2 = gen();         // step u + 2
+    if (half == 0) {
+        load_step(sc, stage0);
+        load_step(sn, stage1);
+        __builtin_amdgcn_s_waitcnt(WAIT_KEEP);  // step 0 has landed
     }
     __syncthreads();
 
-    // Step u, with its K in stage ST = u mod 3, step u - 1's V in stage
-    // (ST + 2) mod 3 and step u + 1 loading into stage (ST + 1) mod 3.  Each
-    // half runs its own copy of the loop, with the phases in its own order, so
-    // that neither path carries the other's registers; both pass the same
-    // barriers in the same order.  Returns false once both the step and the
-    // one before it are past the end.
+    // Step u, with its K in stage ST = u mod 4, step u - 1's V in stage
+    // (ST + 3) mod 4, step u + 1 in flight to stage (ST + 1) mod 4 and step
+    // u + 2 loading into stage (ST + 2) mod 4.  Each half runs its own copy of
+    // the loop, with the phases in its own order, so that neither path carries
+    // the other's registers; both pass the same barriers in the same order.
+    // Returns false once both the step and the one before it are past the end.
     auto run = [&](auto half_tag) __attribute__((always_inline)) {
         constexpr int HF = decltype(half_tag)::value;
         // MFMA phase: PV of step u - 1, then QK^T of step u; the A-waves load
-        // step u + 1 meanwhile.  Without a step u + 1 to load, they reload
-        // step u into the free stage (never read), which keeps the QK^T loop
-        // free of branches.
-        auto mfma_part = [&](const u32x4 *vst, const u32x4 *kst, u32x4 *nst) __attribute__((always_inline)) {
+        // step u + 2 meanwhile (spread over the QK^T MFMAs).
+        auto mfma_part = [&](const u32x4 *vst, const u32x4 *kst, u32x4 *lst) __attribute__((always_inline)) {
             if (act(sp))
                 pv_gemm(vst);
             if (HF == 0) {
-                const bool real = loadable(sn);
                 if (act(sc)) {
-                    s_gemm(kst, plan_step(real ? sn : sc, nst), std::true_type{});
-                } else if (real) {
-                    const DmaPlan d = plan_step(sn, nst);
-#pragma unroll
-                    for (int i = 0; i < G::IPA; ++i)
-                        issue_dma(d, i);
+                    s_gemm(kst, plan_step(loadable(sn2) ? sn2.key0 : Nk, lst), std::true_type{});
+                } else {
+                    load_step(sn2, lst);
                 }
             } else if (act(sc)) {
-                s_gemm(kst, plan_step(sc, nst), std::false_type{});
+                s_gemm(kst, plan_step(0, lst), std::false_type{});
             }
         };
         auto iter = [&](auto stage_tag) __attribute__((always_inline)) -> bool {
             constexpr int ST = decltype(stage_tag)::value;
             if (sc.kt < 0 && sp.kt < 0)
                 return false;
-            u32x4 *const kst = ST == 0 ? stage0 : (ST == 1 ? stage1 : stage2);
-            u32x4 *const nst = ST == 0 ? stage1 : (ST == 1 ? stage2 : stage0);
-            u32x4 *const vst = ST == 0 ? stage2 : (ST == 1 ? stage0 : stage1);
+            u32x4 *const kst = ST == 0 ? stage0 : (ST == 1 ? stage1 : (ST == 2 ? stage2 : stage3));
+            u32x4 *const lst = ST == 0 ? stage2 : (ST == 1 ? stage3 : (ST == 2 ? stage0 : stage1));
+            u32x4 *const vst = ST == 0 ? stage3 : (ST == 1 ? stage0 : (ST == 2 ? stage1 : stage2));
             // phase 1: A computes, B exponentiates; phase 2: the other way round
             if (HF == 0)
-                mfma_part(vst, kst, nst);
+                mfma_part(vst, kst, lst);
             else
                 valu_part(sp);
             __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
             if (HF == 0)
                 valu_part(sc);
             else
-                mfma_part(vst, kst, nst);
-            __syncthreads();  // step u + 1 loaded
+                mfma_part(vst, kst, lst);
+            // step u + 1 has landed (step u + 2 may still be in flight)
+            __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
             sp = sc;
             sc = sn;
-            sn = gen();
+            sn = sn2;
+            sn2 = gen();
             return true;
         };
         for (;;) {
@@ -643,12 +722,16 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
                 break;
             if (!iter(std::integral_constant<int, 2>{}))
                 break;
+            if (!iter(std::integral_constant<int, 3>{}))
+                break;
         }
     };
     if (half == 0)
         run(std::integral_constant<int, 0>{});
     else
         run(std::integral_constant<int, 1>{});
+    __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+    __syncthreads();  // every load landed before the workgroup's LDS is released
 
     // ---- epilogue ----
     const float l_tot = l_run + other_half(l_run);
@@ -706,6 +789,9 @@ hipError_t launch(const FwdParams &p, hipStream_t stream)
 hipError_t launch_fwd_bf16(const FwdParams &p, hipStream_t stream)
 {
     if (p.BM != BM || p.W > MAXW)
+        return hipErrorInvalidValue;
+    // byte offsets within a 64-key step are 32-bit
+    if ((int64_t)p.H * p.D * 2 * HK > INT32_MAX)
         return hipErrorInvalidValue;
     if (p.D == 128 && p.BN == 128)
         return launch<128, 128>(p, stream);
