@@ -55,10 +55,12 @@
 //   ds_read_b64_tr_b16, the LDS transpose read.
 // * 16-byte chunks (K) and 64-byte segments (V) are XOR-swizzled per row,
 //   measured free of bank conflicts for these read patterns.
-// * The live tiles are iterated from registers: the mask words of a row are
-//   held one per lane (two words per lane for up to 128 words), a Skip-List
-//   64 entries at a time, so finding the next tile costs scalar instructions,
-//   not a memory round trip per tile.
+// * The union walk is built once per workgroup, by all its threads, into LDS:
+//   one 16-bit entry per visited tile (the k-tile and which q-tiles visit it),
+//   from the mask words or from the Skip-Lists.  It is then read 64 entries
+//   at a time, one per lane, and stepped with readlane: a single scalar
+//   cursor, no memory round trip per tile, and few scalar registers (the
+//   scalar budget is what the loop runs short of).
 // * Workgroups run in plain order: at any time all XCDs work on the q-tiles of
 //   one or two heads, whose K/V (39 MB per head at 75,600 tokens) then stay in
 //   the 256 MB Infinity Cache, so L2 misses are served there, not by HBM.
@@ -117,128 +119,6 @@ __device__ __forceinline__ void lds_or(uint32_t *p, uint32_t bits)
     const uint32_t a = (uint32_t)(size_t)LDS_VOID(p);
     asm volatile("ds_or_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(bits) : "memory");
 }
-
-// Live k-tiles of one row in visiting order (descending), from the Skip-List
-// (LIST) or from the mask words; `none` for a q-tile that does not exist.
-// Returned values are wave-uniform.
-template <bool LIST>
-struct LiveTiles {
-    uint32_t wlo, whi;     // live bits of mask words `lane` and `lane + 64`
-    uint64_t nzlo, nzhi;   // which words have a live bit
-    int w;                 // word `cur` came from
-    uint32_t cur;          // its live bits not yet returned
-    const int32_t *list;
-    int32_t chunk;         // list entries [idx & ~63, +64), one per lane
-    int cnt, idx;
-    bool none;
-
-    // rdo[j] / rsk[j]: must-do / must-skip tile bits of word lane + 64*j
-    __device__ __forceinline__ void init(const uint32_t *m, const int32_t *l, int tk, bool exists,
-                                         const uint32_t (&rdo)[2], const uint32_t (&rsk)[2])
-    {
-        const int lane = threadIdx.x & 63;
-        none = !exists;
-        list = l;
-        idx = 0;
-        cnt = 0;
-        w = 0;
-        cur = 0;
-        chunk = -1;
-        wlo = whi = 0;
-        nzlo = nzhi = 0;
-        if (none)
-            return;
-        if (LIST) {
-            const int c = __builtin_amdgcn_readfirstlane(l[0]);
-            cnt = c < 0 ? 0 : (c > tk ? tk : c);
-            chunk = lane < cnt ? l[1 + lane] : -1;
-        } else {
-            const int W = (tk + 31) >> 5;
-            auto live = [&](int wi, int j) -> uint32_t {
-                if (wi >= W)
-                    return 0u;
-                uint32_t bits = m ? ~m[wi] : 0xffffffffu;
-                bits = (bits & ~rsk[j]) | rdo[j];
-                if (wi == W - 1 && (tk & 31))
-                    bits &= (1u << (tk & 31)) - 1u;
-                return bits;
-            };
-            wlo = live(lane, 0);
-            whi = live(lane + 64, 1);
-            nzlo = __ballot(wlo != 0u);
-            nzhi = __ballot(whi != 0u);
-            w = W;
-        }
-    }
-    __device__ __forceinline__ int next(int tk)
-    {
-        if (none)
-            return -1;
-        if (LIST) {
-            if (idx >= cnt)
-                return -1;
-            if (idx > 0 && (idx & 63) == 0) {
-                const int lane = threadIdx.x & 63;
-                chunk = idx + lane < cnt ? list[1 + idx + lane] : -1;
-            }
-            const int kt = __builtin_amdgcn_readlane(chunk, idx & 63);
-            ++idx;
-            return (kt >= 0 && kt < tk) ? kt : -1;
-        }
-        while (cur == 0u) {
-            // the highest word below w with a live bit
-            int nw = -1;
-            if (w > 64) {
-                const uint64_t mm = nzhi & (w - 64 >= 64 ? ~0ull : ((1ull << (w - 64)) - 1ull));
-                if (mm)
-                    nw = 127 - __builtin_clzll(mm);
-            }
-            if (nw < 0) {
-                const uint64_t mm = nzlo & (w >= 64 ? ~0ull : ((1ull << w) - 1ull));
-                if (mm)
-                    nw = 63 - __builtin_clzll(mm);
-            }
-            if (nw < 0) {
-                none = true;
-                return -1;
-            }
-            w = nw;
-            cur = (uint32_t)__builtin_amdgcn_readlane((int)(nw < 64 ? wlo : whi), nw & 63);
-        }
-        const int bit = 31 - __builtin_clz(cur);
-        cur &= ~(1u << bit);
-        return w * 32 + bit;
-    }
-};
-
-// The union of two rows' live tiles, descending; flags bit 0 / bit 1 say
-// whether q-tile A / B visits the returned tile.
-template <bool LIST>
-struct LivePair {
-    LiveTiles<LIST> a, b;
-    int na, nb;
-    __device__ __forceinline__ void init(const uint32_t *ma, const int32_t *la, const uint32_t *mb,
-                                         const int32_t *lb, int tk, bool has_b, const uint32_t (&rdo)[2],
-                                         const uint32_t (&rsk)[2])
-    {
-        a.init(ma, la, tk, true, rdo, rsk);
-        b.init(mb, lb, tk, has_b, rdo, rsk);
-        na = a.next(tk);
-        nb = b.next(tk);
-    }
-    __device__ __forceinline__ int next(int &flags, int tk)
-    {
-        const int kt = na > nb ? na : nb;
-        if (kt < 0)
-            return -1;
-        flags = (na == kt ? 1 : 0) | (nb == kt ? 2 : 0);
-        if (na == kt)
-            na = a.next(tk);
-        if (nb == kt)
-            nb = b.next(tk);
-        return kt;
-    }
-};
 
 // One 64-key step of the union walk (wave-uniform).
 struct Step {
@@ -335,6 +215,10 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     __shared__ u32x4 stage2[G::STAGE];
     __shared__ u32x4 stage3[G::STAGE];
     __shared__ uint32_t keep[2][MAXW];
+    __shared__ uint32_t wlive[2][MAXW];   // live tiles of A and B, one bit per k-tile
+    __shared__ int32_t wcnt[MAXW];        // tiles of the union per mask word
+    __shared__ uint16_t walk[MAXW * 32];  // the union walk: k-tile | A visits << 12 | B visits << 13
+    __shared__ int32_t nwalk;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -457,23 +341,71 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         for (int j = 0; j < 8; ++j)
             P[ks][j] = (__bf16)0.f;
 
-    const uint32_t *mrow_a = p.mask_in ? p.mask_in + row_a * W : nullptr;
-    const uint32_t *mrow_b = (p.mask_in && has_b) ? p.mask_in + (row_a + 1) * W : nullptr;
-    const int32_t *list_a = LIST ? p.skiplist + row_a * (1 + Tk) : nullptr;
-    const int32_t *list_b = (LIST && has_b) ? p.skiplist + (row_a + 1) * (1 + Tk) : nullptr;
-    LivePair<LIST> it;
-    // this lane's words (lane, lane + 64) of the per-tile range bits
-    uint32_t rdo[2] = {0u, 0u}, rsk[2] = {0u, 0u};
-    if (ranges && !LIST) {
-        rdo[0] = p.rg.do_bits[lane];
-        rdo[1] = p.rg.do_bits[lane + 64];
-        rsk[0] = p.rg.skip_bits[lane];
-        rsk[1] = p.rg.skip_bits[lane + 64];
+    // ---- the union walk of the two q-tiles, built once into LDS ----
+    // Live tiles per mask word: from the Skip-Lists (LIST) or from mask_in with
+    // the token ranges applied (must-skip tiles out, must-do tiles in).  A
+    // q-tile that does not exist has none.
+    if (tid == 0)
+        nwalk = 0;  // no mask words (no keys): an empty walk
+    if (LIST) {
+        if (tid < 2 * W)
+            wlive[tid / W][tid % W] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) {
+            if (hq == 1 && !has_b)
+                break;
+            const int32_t *l = p.skiplist + (row_a + hq) * (1 + Tk);
+            const int c = min(max(l[0], 0), Tk);
+            for (int i = tid; i < c; i += NT) {
+                const int kt = l[1 + i];
+                if (kt >= 0 && kt < Tk)
+                    atomicOr(&wlive[hq][kt >> 5], 1u << (kt & 31));
+            }
+        }
+    } else if (tid < 2 * W) {
+        const int hq = tid / W, w = tid % W;
+        uint32_t bits = 0u;
+        if (hq == 0 || has_b) {
+            bits = p.mask_in ? ~p.mask_in[(row_a + hq) * W + w] : 0xffffffffu;
+            if (ranges)
+                bits = (bits & ~p.rg.skip_bits[w]) | p.rg.do_bits[w];
+            if (w == W - 1 && (Tk & 31))
+                bits &= (1u << (Tk & 31)) - 1u;
+        }
+        wlive[hq][w] = bits;
     }
-    it.init(mrow_a, list_a, mrow_b, list_b, Tk, has_b, rdo, rsk);
-    int g_fl = 0;
-    int g_kt = it.next(g_fl, Tk);
-    int g_sub = 0;
+    __syncthreads();
+    if (tid < W)
+        wcnt[tid] = __builtin_popcount(wlive[0][tid] | wlive[1][tid]);
+    __syncthreads();
+    if (tid < W) {
+        // descending order: the tiles of the words above this one come first
+        int pos = 0;
+        for (int w = W - 1; w > tid; --w)
+            pos += wcnt[w];
+        const uint32_t a = wlive[0][tid], bb = wlive[1][tid];
+        uint32_t u = a | bb;
+        while (u) {
+            const int bit = 31 - __builtin_clz(u);
+            u &= ~(1u << bit);
+            walk[pos++] = (uint16_t)((tid * 32 + bit) | (((a >> bit) & 1u) << 12) | (((bb >> bit) & 1u) << 13));
+        }
+        if (tid == 0)
+            nwalk = pos;
+    }
+    __syncthreads();
+
+    // The walk is read 64 entries at a time, one per lane, and stepped with
+    // readlane: one scalar cursor, no per-tile memory round trip.
+    const int n_walk = __builtin_amdgcn_readfirstlane(nwalk);
+    int g_idx = 0, g_sub = 0, g_kt = -1, g_fl = 0;
+    uint32_t chunk = lane < n_walk ? walk[lane] : 0u;
+    if (n_walk > 0) {
+        const int e = __builtin_amdgcn_readfirstlane((int)chunk);
+        g_kt = e & 0xfff;
+        g_fl = e >> 12;
+    }
     auto gen = [&]() __attribute__((always_inline)) {
         // wave-uniform by construction; readfirstlane lets the compiler keep
         // the step (and the load addresses built from it) in scalar registers
@@ -484,7 +416,15 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         s.key0 = s.kt * BN + s.sub * HK;
         if (g_kt >= 0 && ++g_sub == SPT) {
             g_sub = 0;
-            g_kt = it.next(g_fl, Tk);
+            if (++g_idx >= n_walk) {
+                g_kt = -1;
+            } else {
+                if ((g_idx & 63) == 0)
+                    chunk = g_idx + lane < n_walk ? walk[g_idx + lane] : 0u;
+                const int e = __builtin_amdgcn_readlane((int)chunk, g_idx & 63);
+                g_kt = e & 0xfff;
+                g_fl = e >> 12;
+            }
         }
         return s;
     };
