@@ -19,13 +19,15 @@
 //   visits, so each q-tile sees exactly its own live tiles in its own order:
 //   decisions and outputs are those of a one-q-tile kernel.  Both q-tiles
 //   read the same K/V from LDS, so one copy of a step serves 256 queries.
-// * Ping-pong: every step is two barrier-separated phases.  In the first,
-//   A's waves run their MFMAs (PV of the previous step, then QK^T of this one)
-//   while B's waves run the softmax of the previous step; in the second the
-//   roles swap.  On every SIMD one wave feeds the matrix core while the other
+// * Ping-pong: within a step, A's waves first run their MFMAs (PV of the
+//   previous step, then QK^T of this one) and then the softmax of this step;
+//   B's waves run the softmax of the previous step first and their MFMAs
+//   after.  On every SIMD one wave then feeds the matrix core while the other
 //   runs its exponentials on the vector ALU, instead of both waves competing
-//   for one unit.  The MFMA phases are software-pipelined by hand: the LDS
-//   reads run four MFMAs ahead of their use.
+//   for one unit.  One barrier per step (the stage hand-over) keeps the
+//   halves in step; a second one between the two halves' roles measured
+//   slower.  The MFMA parts are software-pipelined by hand: the LDS reads run
+//   four MFMAs ahead of their use.
 //
 // gfx950 layout choices
 // * Both contractions are transposed, S^T = K Q^T and O^T = V^T P^T, on
@@ -39,8 +41,8 @@
 // * K and V steps go global -> LDS by direct-to-LDS buffer loads
 //   (buffer_load_dwordx4 ... lds): no staging registers, no LDS store
 //   instructions.  Four LDS stages (128 KB at head_dim 128) and a prefetch
-//   distance of two steps: while step u is computed (its K read in both
-//   phases of step u, its V in both phases of step u + 1), step u + 1 is in
+//   distance of two steps: while step u is computed (its K read by both
+//   halves in step u, its V by both halves in step u + 1), step u + 1 is in
 //   flight and A's waves issue step u + 2 among their QK^T MFMAs.  Each
 //   load's source is a buffer resource (base, byte range) built in scalar
 //   registers per 16 or 32 key rows, so addresses cost no vector
@@ -516,7 +518,7 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         }
     };
 
-    // VALU phase of this wave's q-tile: online softmax of step s (logits in S),
+    // VALU part of this wave's q-tile: online softmax of step s (logits in S),
     // weights into P, then the QK-Skip vote once the whole tile has been seen.
     auto valu_part = [&](const Step &s) __attribute__((always_inline)) {
         if (mine(s) && s.sub == 0) {
@@ -607,12 +609,12 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     // Step u, with its K in stage ST = u mod 4, step u - 1's V in stage
     // (ST + 3) mod 4, step u + 1 in flight to stage (ST + 1) mod 4 and step
     // u + 2 loading into stage (ST + 2) mod 4.  Each half runs its own copy of
-    // the loop, with the phases in its own order, so that neither path carries
-    // the other's registers; both pass the same barriers in the same order.
+    // the loop, with its two parts in its own order, so that neither path
+    // carries the other's registers; both pass the same barrier once per step.
     // Returns false once both the step and the one before it are past the end.
     auto run = [&](auto half_tag) __attribute__((always_inline)) {
         constexpr int HF = decltype(half_tag)::value;
-        // MFMA phase: PV of step u - 1, then QK^T of step u; the A-waves load
+        // MFMA part: PV of step u - 1, then QK^T of step u; the A-waves load
         // step u + 2 meanwhile (spread over the QK^T MFMAs).
         auto mfma_part = [&](const u32x4 *vst, const u32x4 *kst, u32x4 *lst) __attribute__((always_inline)) {
             if (act(sp))
@@ -634,13 +636,13 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
             u32x4 *const kst = ST == 0 ? stage0 : (ST == 1 ? stage1 : (ST == 2 ? stage2 : stage3));
             u32x4 *const lst = ST == 0 ? stage2 : (ST == 1 ? stage3 : (ST == 2 ? stage0 : stage1));
             u32x4 *const vst = ST == 0 ? stage3 : (ST == 1 ? stage0 : (ST == 2 ? stage1 : stage2));
-            // phase 1: A computes, B exponentiates; phase 2: the other way round
+            // A: MFMAs, then softmax; B: softmax, then MFMAs.  No barrier in
+            // between: the opposite orders alone keep one wave of each SIMD on
+            // the matrix core while the other is on the vector ALU.
             if (HF == 0)
                 mfma_part(vst, kst, lst);
             else
                 valu_part(sp);
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
             if (HF == 0)
                 valu_part(sc);
             else
