@@ -114,39 +114,51 @@ fwd_fp32_kernel(FwdParams p)
         }
         __syncthreads();
 
-        double s[TILE];
-        double mloc = -INFINITY;
+        // The tile in two 32-key halves, each folded into the online softmax
+        // (exact in any grouping; half the logits live at a time keeps the
+        // fp64 state in registers).  The QK-Skip test uses the maximum over
+        // the whole tile against the running max taken before it.
+        const double m_before = m_run;
+        double m_tile = -INFINITY;
 #pragma unroll
-        for (int c = 0; c < TILE; ++c) {
-            double dot = 0.0;
+        for (int hc = 0; hc < TILE; hc += TILE / 2) {
+            double s[TILE / 2];
+            double mloc = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < DIM; ++e)
-                dot = fma((double)qv[e], (double)Ks[c][e], dot);
-            s[c] = (key0 + c < Nk) ? dot * scale : -INFINITY;
-            mloc = fmax(mloc, s[c]);
+            for (int c = 0; c < TILE / 2; ++c) {
+                double dot = 0.0;
+#pragma unroll
+                for (int e = 0; e < DIM; ++e)
+                    dot = fma((double)qv[e], (double)Ks[hc + c][e], dot);
+                s[c] = (key0 + hc + c < Nk) ? dot * scale : -INFINITY;
+                mloc = fmax(mloc, s[c]);
+            }
+            m_tile = fmax(m_tile, mloc);
+            const double m_new = fmax(m_run, mloc);
+            if (m_new > -INFINITY) {
+                const double alpha = exp(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int e = 0; e < DIM; ++e)
+                    o[e] *= alpha;
+#pragma unroll
+                for (int c = 0; c < TILE / 2; ++c) {
+                    const double pc = (double)expf((float)(s[c] - m_new));
+                    l_run += pc;
+#pragma unroll
+                    for (int e = 0; e < DIM; ++e)
+                        o[e] = fma(pc, (double)Vs[hc + c][e], o[e]);
+                }
+                m_run = m_new;
+            }
         }
         if (vote) {
             // a must-do tile is never marked
             const bool must_do = ranges && ((p.rg.do_bits[kt >> 5] >> (kt & 31)) & 1u);
-            const bool keep_lane = must_do || (qvalid && !(mloc - m_run < tau));
+            const bool keep_lane = must_do || (qvalid && !(m_tile - m_before < tau));
             if (__ballot(keep_lane) != 0ull && lane == 0)
                 atomicOr(&keep[kt >> 5], 1u << (kt & 31));
         }
-        const double m_new = fmax(m_run, mloc);
-        const double alpha = exp(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int e = 0; e < DIM; ++e)
-            o[e] *= alpha;
-#pragma unroll
-        for (int c = 0; c < TILE; ++c) {
-            const double pc = (double)expf((float)(s[c] - m_new));
-            l_run += pc;
-#pragma unroll
-            for (int e = 0; e < DIM; ++e)
-                o[e] = fma(pc, (double)Vs[c][e], o[e]);
-        }
-        m_run = m_new;
     }
 
     if (qvalid) {
