@@ -272,3 +272,30 @@ def test_sequence_parallel_share_over_a_trajectory():
         err = np.abs(merged.cpu().double().numpy() - ref).max()
         log("  SP share step %d merged err %.4g" % (step, err))
         assert err <= 2e-2
+
+
+@pytest.mark.parametrize("D,BN", [(128, 128), (64, 64)])
+@pytest.mark.parametrize("skiplist", [False, True])
+def test_skipped_tiles_contribute_nothing(D, BN, skiplist):
+    """Full-Stage Elimination: a k-tile set in mask_in is bypassed entirely, so
+    its keys and values are never read.  Tiles skipped by every row get NaN K
+    and V; outputs, lse and marks must equal the oracle's on the clean tensors
+    (the q-tiles of a workgroup share K/V loads, so a tile that any row visits
+    would be loaded; one that no row visits must not even be touched)."""
+    q, k, v = tokens((6, 10, 16), 2, head_dim=D)                     # N = 960
+    N = q.shape[1]
+    Tq, Tk = -(-N // 128), -(-N // BN)
+    rows = 2 * Tq
+    mask = rand_mask(rows, Tk, 0.3, seed=17)
+    dead = [1, Tk // 2, Tk - 2]
+    for kt in dead:
+        mask[:, kt >> 5] |= np.uint32(1 << (kt & 31))
+    kp, vp = k.clone(), v.clone()
+    for kt in dead:
+        kp[:, kt * BN:(kt + 1) * BN] = float("nan")
+        vp[:, kt * BN:(kt + 1) * BN] = float("nan")
+    scale = 1.0 / math.sqrt(D)
+    orc = oracle.fwd(q, k, v, 128, BN, -3.0, scale, mask_in=mask)
+    gpu = pa.gpu_fwd(q, kp, vp, 128, BN, -3.0, scale, mask_in=mask, use_skiplist=skiplist)
+    stats = pa.compare_rows(gpu, orc, orc["rows"], 1, N, 2, 128, BN, -3.0, q.dtype)
+    log("  D %d BN %d skiplist %s dead tiles %s" % (D, BN, skiplist, dead), stats)

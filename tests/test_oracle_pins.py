@@ -104,6 +104,23 @@ def test_fully_skipped_row_gives_zero_and_minus_inf():
     assert np.array_equal(oc.bits_of(r["mask_out"], 2), bits)
 
 
+def test_skipped_tiles_are_never_read():
+    """Full-Stage Elimination (README): a skipped tile costs no K/V traffic, so
+    NaN keys and values in tiles that every row skips change nothing."""
+    q, k, v = oc.random_case(5, 1, 40, 2, 8)
+    rng = np.random.default_rng(3)
+    bits = rng.random((10, 5)) < 0.3
+    bits[:, 2] = True
+    words = oc.words_of(bits)
+    kp, vp = k.clone(), v.clone()
+    kp[:, 16:24] = float("nan")
+    vp[:, 16:24] = float("nan")
+    a = oracle.fwd(q, k, v, 8, 8, -2.0, 0.4, mask_in=words)
+    b = oracle.fwd(q, kp, vp, 8, 8, -2.0, 0.4, mask_in=words)
+    for key in ("out", "lse", "mask_out", "margin"):
+        assert np.array_equal(np.asarray(a[key]), np.asarray(b[key]), equal_nan=True), key
+
+
 def test_bits_past_last_tile_are_cleared():
     q, k, v = oc.random_case(2, 1, 40, 1, 4)     # Tk = 5 with 8-wide tiles
     words = np.full((5, 1), 0xFFFFFFE0, np.uint32)  # only padding bits set
