@@ -171,9 +171,9 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const char *base, uint32_t bytes)
 }
 
 // LDS layout of one 64-key step.  K and V arrive by direct-to-LDS loads
-// (global_load_lds_dwordx4): each wave instruction writes 64 consecutive
+// (buffer_load_dwordx4 ... lds): each wave instruction writes 64 consecutive
 // 16-byte chunks, lane i to chunk i, so the layout is any permutation of the
-// step's chunks -- chosen per lane by the global address it loads.
+// step's chunks -- chosen per lane by the byte offset it loads.
 // K: key x head-dim with the kperm row order; chunk c of LDS row r holds
 //    head-dim chunk c ^ fk(r).  The MFMA A-operand reads (16-byte, 16 lanes
 //    per LDS cycle over 32 consecutive rows) then hit 16 distinct 16-byte bank
