@@ -30,8 +30,8 @@
  *       - skipped tiles are never visited and do not move m_run;
  *       - a newly marked tile still counts in this step's output and is
  *         skipped from the next step on ([README] "QK-Skip Algorithm": the
- *         Skip-Mask is updated each timestep and marked tiles are bypassed
- *         in subsequent timesteps);
+ *         mask is refreshed every denoising step, and a tile marked at one
+ *         step drops out from the following steps);
  *       - mask_out = mask_in OR newly-marked: marks are never removed;
  *       - keys >= Nk do not exist (excluded from every max and sum);
  *         query rows >= Nq do not vote and are not written;
