@@ -351,3 +351,176 @@ def check_ranges(lib=None):
 
 ALL_CHECKS = (run_golden, check_dense, check_masked_and_rule, check_tile_invariance, check_edge_cases,
               check_nonsquare, check_ranges)
+
+
+# ---- checks of the oracle's Python helpers (Skip-List reference, tile flags,
+# LSE merge, error budgets, calibration).  They look the oracle up through this
+# module's global, so a test can substitute a variant of it.
+
+def check_tile_flags():
+    """The tile sets derived by hand from the README's range examples."""
+    fails = []
+    for case in load_range_golden()["cases"]:
+        do, sk = oracle.tile_flags(case["N"], case["BN"], case.get("must_do"), case.get("must_skip"))
+        if np.flatnonzero(do).tolist() != case.get("must_do_tiles", []):
+            fails.append("tile_flags must-do: " + case["name"])
+        if np.flatnonzero(sk).tolist() != case.get("must_skip_tiles", []):
+            fails.append("tile_flags must-skip: " + case["name"])
+    return fails
+
+
+def check_skiplist():
+    """Skip-List reference: exactly the clear bits of each row, last tile
+    first, across word boundaries; must-do beats a mark and must-skip,
+    must-skip drops an unmarked tile."""
+    fails = []
+    rng = np.random.default_rng(0)
+    for tk in (1, 5, 31, 32, 33, 70):
+        bits = rng.random((6, tk)) < 0.4
+        counts, lists = oracle.skiplist(words_of(bits), tk)
+        for r in range(6):
+            if counts[r] != (~bits[r]).sum() or list(lists[r]) != sorted(np.flatnonzero(~bits[r]).tolist(),
+                                                                          reverse=True):
+                fails.append("skiplist: Tk %d row %d" % (tk, r))
+                break
+    do = np.array([True, False, False, True, False])
+    sk = np.array([False, True, False, True, False])
+    bits = np.array([[1, 0, 0, 1, 0], [0, 0, 1, 0, 1]], bool)
+    counts, lists = oracle.skiplist(words_of(bits), 5, do, sk)
+    # row 0: 3 is must-do (beats its mark and its must-skip), 1 is must-skip
+    # row 1: 4 and 2 are marked, 1 is must-skip
+    if [list(x) for x in lists] != [[4, 3, 2, 0], [3, 0]] or list(counts) != [4, 2]:
+        fails.append("skiplist with tile flags")
+    return fails
+
+
+def check_merge():
+    """LSE merge: attention over a partition of the keys, merged, is attention
+    over all keys (brute force), also through the oracle forward with an empty
+    part; all parts empty give 0 and -inf; shifting every part's lse by the
+    same constant (far outside exp's range) shifts the result and leaves the
+    output unchanged."""
+    fails = []
+    g = torch.Generator().manual_seed(21)
+    B, Nq, Nk, H, D = 2, 30, 70, 2, 8
+    q = 1.5 * torch.randn(B, Nq, H, D, generator=g, dtype=torch.float64)
+    k = 1.5 * torch.randn(B, Nk, H, D, generator=g, dtype=torch.float64)
+    v = torch.randn(B, Nk, H, D, generator=g, dtype=torch.float64)
+    scale = 0.4
+    o_ref, lse_ref, _ = dense_reference(q, k, v, scale)
+    lse_ref = np.transpose(lse_ref, (0, 2, 1))                    # [B, Nq, H] to match out[..., :]
+    outs, lses = [], []
+    for a, b in zip([0, 16, 17, 48], [16, 17, 48, 70]):
+        o, lse, _ = dense_reference(q, k[:, a:b], v[:, a:b], scale)
+        outs.append(o)
+        lses.append(np.transpose(lse, (0, 2, 1)))
+    out, lse = oracle.merge(outs, lses)
+    if not (np.allclose(out, o_ref, atol=1e-12) and np.allclose(lse, lse_ref, atol=1e-12)):
+        fails.append("merge of key splits is not full attention")
+    with np.errstate(over="ignore", invalid="ignore"):
+        for c in (1000.0, -1000.0):
+            out2, lse2 = oracle.merge(outs, [x + c for x in lses])
+            if not (np.allclose(out2, o_ref, atol=1e-12) and np.allclose(lse2, lse_ref + c, atol=1e-9)):
+                fails.append("merge is not shift invariant (shift %g)" % c)
+    outs, lses = [], []
+    for a, b in ((0, 32), (32, 32), (32, 70)):
+        r = oracle.fwd(q, k[:, a:b], v[:, a:b], 8, 16, -math.inf, scale)
+        o, l = oracle.unpack_rows(r, B, Nq, H, 8)
+        outs.append(o)
+        lses.append(np.transpose(l, (0, 2, 1)))
+    out, lse = oracle.merge(outs, lses)
+    if not (np.allclose(out, o_ref, atol=1e-12) and np.allclose(lse, lse_ref, atol=1e-12)):
+        fails.append("merge of forward partials with an empty part")
+    out, lse = oracle.merge([np.ones((3, 4))] * 2, [np.full(3, -np.inf)] * 2)
+    if not (np.all(out == 0) and np.all(np.isneginf(lse))):
+        fails.append("merge of empty parts")
+    return fails
+
+
+def check_error_budgets():
+    """[README] Error Calibration: over the first int(T*ratio) steps the
+    multiplier goes 0.5 + 0.5*t/int(T*ratio); later steps get 1.0."""
+    fails = []
+    b = oracle.error_budgets(50, 0.3)
+    if not (len(b) == 50 and b[0] == 0.5 and b[1] == 0.5 + 0.5 / 15 and b[14] == 0.5 + 0.5 * 14 / 15
+            and all(x == 1.0 for x in b[15:]) and b[:15] == sorted(b[:15])):
+        fails.append("error budgets, 50 steps")
+    if oracle.error_budgets(3, 0.3) != [1.0, 1.0, 1.0]:                 # int(0.9) = 0 early steps
+        fails.append("error budgets, 3 steps")
+    if oracle.error_budgets(10, 0.5)[:5] != [0.5, 0.6, 0.7, 0.8, 0.9]:
+        fails.append("error budgets, 10 steps")
+    return fails
+
+
+def calib_inputs(steps=3, N=96, H=2, D=8, seed=0):
+    """A tiny drifting trajectory with a locality bias, so thresholds matter."""
+    g = torch.Generator().manual_seed(seed)
+    pos = torch.arange(N, dtype=torch.float64)
+    feat = torch.stack([torch.cos(pos / 6.0 * (j + 1)) for j in range(D)], -1)    # smooth in the position
+    q0 = 3.0 * feat[None, :, None, :].expand(1, N, H, D) + torch.randn(1, N, H, D, generator=g, dtype=torch.float64)
+    k0 = 3.0 * feat[None, :, None, :].expand(1, N, H, D) + torch.randn(1, N, H, D, generator=g, dtype=torch.float64)
+    v0 = torch.randn(1, N, H, D, generator=g, dtype=torch.float64)
+    out = []
+    for t in range(steps):
+        out.append((q0 + 0.05 * t * torch.randn(1, N, H, D, generator=g, dtype=torch.float64),
+                    k0 + 0.05 * t * torch.randn(1, N, H, D, generator=g, dtype=torch.float64), v0))
+    return out
+
+
+def check_calibration():
+    """Re-evaluated by brute force at every step: the chosen tau's error is
+    within its budget and every larger candidate's is not (numpy attention over
+    the visited tiles against numpy dense attention, with the mask carried from
+    the earlier steps); an unbounded budget takes the largest candidate and a
+    zero budget lets no new mark change the output."""
+    fails = []
+    steps = calib_inputs()
+    BM = BN = 16
+    taus = [0.0, -1.0, -2.0, -3.0, -5.0, -8.0]
+    scale = 0.35
+    # ratio 0.67 over 3 steps: int(2.01) = 2 early steps, multipliers 0.5, 0.75, 1.0
+    res = oracle.calibrate(steps, BM, BN, scale, base_error=0.02, taus=taus, early_step_ratio=0.67)
+    budgets = [0.5, 0.75, 1.0]
+    mask = np.zeros((2 * 6, 1), np.uint32)
+    saw_skip = False
+    for t, ((q, k, v), r) in enumerate(zip(steps, res)):
+        if r["budget"] != 0.02 * budgets[t]:
+            fails.append("calibration budget, step %d" % t)
+        o_dense, _, _ = dense_reference(q, k, v, scale)
+        norm = np.sqrt((o_dense ** 2).sum())
+        for tau in sorted(taus + [-math.inf], reverse=True):
+            m2 = oracle.fwd(q, k, v, BM, BN, tau, scale, mask_in=mask)["mask_out"]
+            o2, _, _ = dense_reference(q, k, v, scale, bits_of(m2, 6), BM, BN)
+            err = np.sqrt(((o2 - o_dense) ** 2).sum()) / norm
+            if tau > r["tau"]:
+                if err <= r["budget"]:
+                    fails.append("calibration skipped a feasible larger tau %g, step %d" % (tau, t))
+            elif tau == r["tau"]:
+                if abs(err - r["error"]) > 1e-12 or not (err <= r["budget"] or tau == -math.inf):
+                    fails.append("calibration error of the chosen tau, step %d" % t)
+                if not np.array_equal(np.asarray(r["mask"]).view(np.uint32), m2):
+                    fails.append("calibration carries the wrong mask, step %d" % t)
+                break
+        saw_skip = saw_skip or r["sparsity"] > 0
+        mask = np.asarray(r["mask"]).view(np.uint32)
+    if not saw_skip:
+        fails.append("calibration never marked a tile")
+    steps = calib_inputs(steps=2)
+    taus = [0.0, -2.0, -6.0]
+    if [r["tau"] for r in oracle.calibrate(steps, 16, 16, 0.35, math.inf, taus)] != [0.0, 0.0]:
+        fails.append("calibration with an unbounded budget")
+    if any(r["error"] != 0.0 for r in oracle.calibrate(steps, 16, 16, 0.35, 0.0, taus)):
+        fails.append("calibration with a zero budget")
+    # marks accumulate across steps: a second step whose keys sit half a
+    # sequence away from the first's keeps every mark the first step made
+    (q, k, v), _ = steps
+    moved = (q, torch.roll(k, 48, dims=1), torch.roll(v, 48, dims=1))
+    res = oracle.calibrate([(q, k, v), moved], 16, 16, 0.35, math.inf, taus)
+    b0, b1 = bits_of(res[0]["mask"], 6), bits_of(res[1]["mask"], 6)
+    want = oracle.fwd(*moved, 16, 16, 0.0, 0.35, mask_in=res[0]["mask"])["mask_out"]
+    if not b0.any() or np.any(b0 & ~b1) or not np.array_equal(np.asarray(res[1]["mask"]).view(np.uint32), want):
+        fails.append("calibration does not carry the marks of earlier steps")
+    return fails
+
+
+PY_CHECKS = (check_tile_flags, check_skiplist, check_merge, check_error_budgets, check_calibration)

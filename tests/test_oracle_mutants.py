@@ -1,6 +1,7 @@
-"""Plant plausible mistakes in copies of the oracle's C source and require the
+"""Plant plausible mistakes in copies of the oracle's C source and Python helpers and require the
 independent checks (tests/oracle_checks.py) to catch every one.  CPU only."""
 
+import importlib.util
 import os
 import subprocess
 
@@ -62,6 +63,64 @@ def test_planted_mistake_is_caught(name, old, new, tmp_path):
     fails = []
     for check in oc.ALL_CHECKS:
         fails += check(lib=lib)
+        if fails:
+            break
+    assert fails, "planted mistake not caught: " + name
+
+
+PY_SRC = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.py")).read()
+
+# (name, text in oracle.py, planted replacement) -- mistakes in the Python helpers
+PY_MUTANTS = [
+    ("skip-list ascending", "for kt in range(tk - 1, -1, -1):\n            marked", "for kt in range(tk):\n            marked"),
+    ("skip-list reads word 0 only", "marked = (int(m[r, kt // 32]) >> (kt % 32)) & 1",
+     "marked = (int(m[r, 0]) >> (kt % 32)) & 1"),
+    ("skip-list must-skip beats must-do", "if do or not (marked or sk):", "if (do and not sk) or not (marked or sk):"),
+    ("skip-list must-do ignored", "if do or not (marked or sk):", "if not (marked or sk):"),
+    ("tile flags end inclusive", "range(max(end + 1, 0), min(start, nk - 1) + 1)",
+     "range(max(end, 0), min(start, nk - 1) + 1)"),
+    ("tile flags start exclusive", "range(max(end + 1, 0), min(start, nk - 1) + 1)",
+     "range(max(end + 1, 0), min(start, nk - 1))"),
+    ("tile flags must-skip on any key", "cs[kt * tile_n:(kt + 1) * tile_n].all()", "cs[kt * tile_n:(kt + 1) * tile_n].any()"),
+    ("tile flags last key of a tile dropped", "cd[kt * tile_n:(kt + 1) * tile_n].any()",
+     "cd[kt * tile_n:(kt + 1) * tile_n - 1].any()"),
+    ("merge without normalisation", "out = (w[..., None] * O).sum(axis=0) / np.where(empty, 1.0, s)[..., None]",
+     "out = (w[..., None] * O).sum(axis=0)"),
+    ("merge without the max shift", "m_safe = np.where(empty, 0.0, m)", "m_safe = np.where(empty, 0.0, 0.0 * m)"),
+    ("merge lse is the max", "lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, s)))",
+     "lse = np.where(empty, -np.inf, m_safe)"),
+    ("merge weights by lse, not exp", "w = np.exp(L - m_safe)", "w = np.where(np.isneginf(L), 0.0, np.exp(L - m_safe) * 0 + 1)"),
+    ("budgets reach 1.0 inside the early steps", "0.5 + 0.5 * (t / n_early)", "0.5 + 0.5 * (t / max(n_early - 1, 1))"),
+    ("budgets rounded early count", "n_early = int(num_steps * early_step_ratio)", "n_early = round(num_steps * early_step_ratio)"),
+    ("budgets loosest first", "0.5 + 0.5 * (t / n_early)", "1.0 - 0.5 * (t / n_early)"),
+    ("calibration takes the smallest feasible tau", "cands = sorted(set(float(t) for t in taus), reverse=True)",
+     "cands = sorted(set(float(t) for t in taus))"),
+    ("calibration forgets the carried mask", "        mask = m2\n    return out", "        mask = None\n    return out"),
+    ("calibration error unnormalised", "err = float(np.sqrt(((o2 - od) ** 2).sum())) / norm if norm > 0 else 0.0",
+     "err = float(np.sqrt(((o2 - od) ** 2).sum()))"),
+    ("calibration budget unscaled", "budget = base_error * mult[t]", "budget = base_error"),
+    ("calibration error before the marks take effect",
+     "r2 = fwd(q, k, v, tile_m, tile_n, -math.inf, scale, mask_in=m2, want_mask_out=False, nthreads=nthreads)",
+     "r2 = fwd(q, k, v, tile_m, tile_n, -math.inf, scale, mask_in=mask, want_mask_out=False, nthreads=nthreads)"),
+    ("unpack swaps heads and q-tiles", "        qt = row % Tq\n        h = (row // Tq) % H",
+     "        h = row % H\n        qt = (row // H) % Tq"),
+]
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
+@pytest.mark.parametrize("name,old,new", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_planted_python_mistake_is_caught(name, old, new, tmp_path, monkeypatch):
+    assert PY_SRC.count(old) >= 1, "mutation site not found: " + name
+    src = tmp_path / "oracle_mutant.py"
+    src.write_text(PY_SRC.replace(old, new, 1))
+    spec = importlib.util.spec_from_file_location("oracle_mutant", str(src))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod._lib = oracle._load()              # the unmodified fp64 C core
+    monkeypatch.setattr(oc, "oracle", mod)
+    fails = []
+    for check in oc.PY_CHECKS + oc.ALL_CHECKS:
+        fails += check()
         if fails:
             break
     assert fails, "planted mistake not caught: " + name

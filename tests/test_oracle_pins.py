@@ -136,14 +136,10 @@ def test_rejects_nan_threshold_and_bad_scale():
         oracle.fwd(q, k, v, 4, 4, -3.0, 0.0)
 
 
-def test_skiplist_reference_round_trip():
-    rng = np.random.default_rng(0)
-    for tk in (1, 5, 31, 32, 33, 70):
-        bits = rng.random((6, tk)) < 0.4
-        counts, lists = oracle.skiplist(oc.words_of(bits), tk)
-        for r in range(6):
-            assert counts[r] == (~bits[r]).sum()
-            assert list(lists[r]) == sorted(np.flatnonzero(~bits[r]).tolist(), reverse=True)
+def test_skiplist_reference():
+    """Skip-List reference: the clear bits of each row, last tile first, across
+    word boundaries; must-do and must-skip tile flags applied."""
+    assert oc.check_skiplist() == []
 
 
 def test_c1_trajectory_masks_grow_and_stay_nondegenerate():
@@ -187,120 +183,21 @@ def test_must_do_and_must_skip_ranges():
 def test_tile_flags_match_the_hand_derived_examples():
     """The Python tile-flag helper (used by the Skip-List reference) gives the
     tile sets derived by hand from the README's examples."""
-    for case in oc.load_range_golden()["cases"]:
-        do, sk = oracle.tile_flags(case["N"], case["BN"], case.get("must_do"), case.get("must_skip"))
-        assert np.flatnonzero(do).tolist() == case.get("must_do_tiles", []), case["name"]
-        assert np.flatnonzero(sk).tolist() == case.get("must_skip_tiles", []), case["name"]
-
-
-def test_skiplist_reference_with_ranges():
-    do = np.array([True, False, False, True, False])
-    sk = np.array([False, True, False, True, False])
-    bits = np.array([[1, 0, 0, 1, 0], [0, 0, 1, 0, 1]], bool)
-    counts, lists = oracle.skiplist(oc.words_of(bits), 5, do, sk)
-    assert list(lists[0]) == [4, 3, 2, 0]     # 3 must-do beats its mark and must-skip; 1 must-skip
-    assert list(lists[1]) == [3, 0]           # 4 and 2 marked, 1 must-skip
-    assert list(counts) == [4, 2]
+    assert oc.check_tile_flags() == []
 
 
 def test_lse_merge_of_key_splits_is_full_attention():
     """Attention over a partition of the keys, merged by LSE, is attention over
     all keys -- by brute force; also through the oracle's own forward on the
     K/V splits (the sequence-parallel use), with a part left empty."""
-    g = torch.Generator().manual_seed(21)
-    B, Nq, Nk, H, D = 2, 30, 70, 2, 8
-    q = 1.5 * torch.randn(B, Nq, H, D, generator=g, dtype=torch.float64)
-    k = 1.5 * torch.randn(B, Nk, H, D, generator=g, dtype=torch.float64)
-    v = torch.randn(B, Nk, H, D, generator=g, dtype=torch.float64)
-    scale = 0.4
-    o_ref, lse_ref, _ = oc.dense_reference(q, k, v, scale)
-    cuts = [0, 16, 17, 48, 70]
-    outs, lses = [], []
-    for a, b in zip(cuts[:-1], cuts[1:]):
-        o, lse, _ = oc.dense_reference(q, k[:, a:b], v[:, a:b], scale)
-        outs.append(o)
-        lses.append(np.transpose(lse, (0, 2, 1)))          # [B, Nq, H] to match out[..., :]
-    out, lse = oracle.merge(outs, lses)
-    assert np.allclose(out, o_ref, atol=1e-12) and np.allclose(lse, np.transpose(lse_ref, (0, 2, 1)), atol=1e-12)
-    # through the oracle forward, per split, with an empty split
-    outs, lses = [], []
-    for a, b in ((0, 32), (32, 32), (32, 70)):
-        r = oracle.fwd(q, k[:, a:b], v[:, a:b], 8, 16, -math.inf, scale)
-        o, l = oracle.unpack_rows(r, B, Nq, H, 8)
-        outs.append(o)
-        lses.append(np.transpose(l, (0, 2, 1)))
-    out, lse = oracle.merge(outs, lses)
-    assert np.allclose(out, o_ref, atol=1e-12)
-    # every part empty: 0 and -inf
-    out, lse = oracle.merge([np.ones((3, 4))] * 2, [np.full(3, -np.inf)] * 2)
-    assert np.all(out == 0) and np.all(np.isneginf(lse))
+    assert oc.check_merge() == []
 
 
 def test_error_budgets_follow_the_printed_schedule():
-    """[README] Error Calibration: over the first int(T*ratio) steps the
-    multiplier goes 0.5 + 0.5*t/int(T*ratio); later steps get 1.0."""
-    b = oracle.error_budgets(50, 0.3)
-    assert len(b) == 50
-    assert b[0] == 0.5
-    assert b[1] == 0.5 + 0.5 / 15
-    assert b[14] == 0.5 + 0.5 * 14 / 15
-    assert all(x == 1.0 for x in b[15:])
-    assert b[:15] == sorted(b[:15])
-    assert oracle.error_budgets(3, 0.3) == [1.0, 1.0, 1.0]    # int(0.9) = 0 early steps
-    assert oracle.error_budgets(10, 0.5)[:5] == [0.5, 0.6, 0.7, 0.8, 0.9]
-
-
-def _calib_inputs(steps=3, N=96, H=2, D=8, seed=0):
-    """A tiny drifting trajectory with a locality bias, so thresholds matter."""
-    g = torch.Generator().manual_seed(seed)
-    pos = torch.arange(N, dtype=torch.float64)
-    feat = torch.stack([torch.cos(pos / 6.0 * (j + 1)) for j in range(D)], -1)    # smooth in the position
-    q0 = 3.0 * feat[None, :, None, :].expand(1, N, H, D) + torch.randn(1, N, H, D, generator=g, dtype=torch.float64)
-    k0 = 3.0 * feat[None, :, None, :].expand(1, N, H, D) + torch.randn(1, N, H, D, generator=g, dtype=torch.float64)
-    v0 = torch.randn(1, N, H, D, generator=g, dtype=torch.float64)
-    out = []
-    for t in range(steps):
-        out.append((q0 + 0.05 * t * torch.randn(1, N, H, D, generator=g, dtype=torch.float64),
-                    k0 + 0.05 * t * torch.randn(1, N, H, D, generator=g, dtype=torch.float64), v0))
-    return out
+    assert oc.check_error_budgets() == []
 
 
 def test_calibration_picks_the_largest_feasible_threshold():
-    """Re-evaluated by brute force at every step: the chosen tau's error is
-    within the budget and every larger candidate's is not (numpy attention over
-    the visited tiles, against numpy dense attention)."""
-    steps = _calib_inputs()
-    BM = BN = 16
-    taus = [0.0, -1.0, -2.0, -3.0, -5.0, -8.0]
-    scale = 0.35
-    res = oracle.calibrate(steps, BM, BN, scale, base_error=0.02, taus=taus)
-    budgets = oracle.error_budgets(len(steps))
-    mask = np.zeros((2 * 6, 1), np.uint32)
-    saw_skip = False
-    for t, ((q, k, v), r) in enumerate(zip(steps, res)):
-        assert r["budget"] == 0.02 * budgets[t]
-        o_dense, _, _ = oc.dense_reference(q, k, v, scale)
-        norm = np.sqrt((o_dense ** 2).sum())
-        for tau in sorted(taus + [-math.inf], reverse=True):
-            m2 = oracle.fwd(q, k, v, BM, BN, tau, scale, mask_in=mask)["mask_out"]
-            o2, _, _ = oc.dense_reference(q, k, v, scale, oc.bits_of(m2, 6), BM, BN)
-            err = np.sqrt(((o2 - o_dense) ** 2).sum()) / norm
-            if tau > r["tau"]:
-                assert err > r["budget"], (t, tau)
-            elif tau == r["tau"]:
-                assert abs(err - r["error"]) < 1e-12
-                assert err <= r["budget"] or tau == -math.inf
-                break
-        saw_skip = saw_skip or r["sparsity"] > 0
-        mask = r["mask"]
-    assert saw_skip
-
-
-def test_calibration_limits():
-    steps = _calib_inputs(steps=2)
-    taus = [0.0, -2.0, -6.0]
-    # an unbounded budget always takes the most aggressive candidate
-    assert [r["tau"] for r in oracle.calibrate(steps, 16, 16, 0.35, math.inf, taus)] == [0.0, 0.0]
-    # a zero budget never lets a new mark change the output
-    for r in oracle.calibrate(steps, 16, 16, 0.35, 0.0, taus):
-        assert r["error"] == 0.0
+    """Brute-force re-evaluation of every step's choice, plus the unbounded
+    and zero budgets."""
+    assert oc.check_calibration() == []
