@@ -1,0 +1,94 @@
+"""HIP-graph capture of the per-layer step.
+
+The library allocates nothing, clears memory with fill kernels (no
+hipMemsetAsync) and makes no host-synchronising call, so one denoising step
+of a layer -- Skip-List build from the mask, then the forward that reads the
+mask and marks into it in place -- can be captured once and replayed every
+step.  Each replay runs on the step's inputs copied into the captured
+buffers, with eager work and a synchronisation between replays, and must give
+exactly what the eager calls give at the same step (every kernel here is
+deterministic: one workgroup per output row, no atomics on outputs).  A
+second graph captures reset + forward: eager calls between its replays grow
+the mask, and the captured reset has to clear it every time.
+"""
+
+import sys
+
+import pytest
+import torch
+
+from temporal_block_sparse_amd import configs, synth
+from temporal_block_sparse_amd import lite_attn as la
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("bf16 d64 128x64 skiplist", configs.scaled(configs.C2, (4, 10, 25), heads=3, batch=1, steps=4), True),
+    ("bf16 d128 128x128 mask", configs.scaled(configs.C3, (3, 10, 30), heads=2, batch=1, steps=4), False),
+    ("fp32 d64 64x64 mask", configs.scaled(configs.C1, (4, 8, 20), heads=2, batch=1, steps=4), False),
+]
+
+
+def _steps(wl):
+    tr = synth.Trajectory(wl, "cpu")
+    out = []
+    for s in range(wl.steps):
+        if s:
+            tr.advance()
+        out.append(tuple(t.to("cuda") for t in tr.tensors()))
+    return out
+
+
+@pytest.mark.parametrize("name,wl,use_skiplist", CASES, ids=[c[0] for c in CASES])
+def test_graph_replays_equal_eager_steps(name, wl, use_skiplist):
+    print("  %s: N %d H %d d %d tile %dx%d steps %d" % (name, wl.seqlen, wl.heads, wl.head_dim, wl.tile_m,
+                                                       wl.tile_n, wl.steps), flush=True)
+    sys.stdout.flush()
+    steps = _steps(wl)
+    kw = dict(threshold=-3.0, tile_m=wl.tile_m, tile_n=wl.tile_n, use_skiplist=use_skiplist)
+
+    # eager reference: one layer over the trajectory
+    ref = la.LiteAttention(**kw)
+    eager = []
+    for q, k, v in steps:
+        o, l = ref(q, k, v, return_softmax_lse=True)
+        eager.append((o.clone(), l.clone(), ref.mask.clone()))
+    torch.cuda.synchronize()
+    assert (eager[-1][2] != 0).any(), "the trajectory marks nothing; the test would not see the mask carried"
+
+    # the same layer, captured once
+    qs, ks, vs = (t.clone() for t in steps[0])
+    attn = la.LiteAttention(**kw)
+    attn._state_for(qs, ks)                    # mask (and Skip-List) allocated and cleared before capture
+    out = torch.empty_like(qs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _, lse = attn(qs, ks, vs, out=out, return_softmax_lse=True)
+    for s, (q, k, v) in enumerate(steps):
+        qs.copy_(q)
+        ks.copy_(k)
+        vs.copy_(v)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[s][0]), "%s: output differs at step %d" % (name, s)
+        assert torch.equal(lse, eager[s][1]), "%s: lse differs at step %d" % (name, s)
+        assert torch.equal(attn.mask, eager[s][2]), "%s: mask differs at step %d" % (name, s)
+
+    # reset + forward captured together; eager calls in between grow the mask
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        attn.reset_skip_state()
+        attn(qs, ks, vs, out=out)
+    for r in range(3):
+        qs.copy_(steps[0][0])
+        ks.copy_(steps[0][1])
+        vs.copy_(steps[0][2])
+        g2.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[0][0]), "%s: reset+forward replay %d output" % (name, r)
+        assert torch.equal(attn.mask, eager[0][2]), "%s: reset+forward replay %d mask" % (name, r)
+        for q, k, v in steps[1:]:
+            attn(q, k, v)                      # eager steps on the same mask
+        torch.cuda.synchronize()
+        assert torch.equal(attn.mask, eager[-1][2])
