@@ -177,6 +177,7 @@ int lite_attn_fwd(const lite_attn_desc *desc, const void *q, const void *k, cons
  *   mask      device, lite_attn_mask_words() uint32 (NULL = nothing skipped).
  *   skiplist  device, lite_attn_skiplist_len() int32; must not overlap mask.
  *   ranges    host, or NULL: the ranges the forward will be called with.
+ * Tk > 4096 is LITE_ERR_UNSUPPORTED, as for the forward.
  */
 int lite_attn_build_skiplist(const lite_attn_desc *desc, const uint32_t *mask, int32_t *skiplist,
                              const lite_attn_ranges *ranges, void *stream);

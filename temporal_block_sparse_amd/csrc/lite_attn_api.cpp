@@ -305,6 +305,8 @@ int lite_attn_build_skiplist(const lite_attn_desc *desc, const uint32_t *mask, i
     int rc = check_desc(desc, &r);
     if (rc != LITE_OK)
         return rc;
+    if (r.Tk > 32 * lite_attn::MAX_TILE_WORDS)
+        return LITE_ERR_UNSUPPORTED;  // the documented bound on k-tiles, as for the forward
     lite_attn::TileRanges rg;
     rc = tile_ranges(ranges, desc->seqlen_kv, desc->tile_n, r.Tk, &rg);
     if (rc != LITE_OK)

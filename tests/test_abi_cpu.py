@@ -142,6 +142,9 @@ def test_skiplist_and_reset_validation():
     assert la.LIB.lite_attn_build_skiplist(ctypes.byref(d), ctypes.c_void_p(m), ctypes.c_void_p(m + 8), None, None) == 7
     assert la.LIB.lite_attn_reset_mask(ctypes.byref(d), ctypes.c_void_p(m + 1), None) == 6
     assert la.LIB.lite_attn_reset_mask(ctypes.byref(desc(tile_m=-3)), ctypes.c_void_p(m), None) == 2
+    # more than 4096 k-tiles: unsupported for the Skip-List build too (checked before any pointer)
+    assert la.LIB.lite_attn_build_skiplist(ctypes.byref(desc(seqlen=4097 * 128)), ctypes.c_void_p(m),
+                                           ctypes.c_void_p(FAKE + (1 << 30)), None, None) == 3
 
 
 def test_binding_raises_with_code():
