@@ -3,21 +3,27 @@
 // Algorithm", "Full-Stage Elimination", reverse iteration over k-tiles), for
 // callers that keep activations in fp32.
 //
-// One workgroup of 8 waves per (batch, head, q-tile); lane = query in every
-// wave.  Per visited k-tile, the waves split the work three ways:
-//   logits  -- wave w computes keys 8w .. 8w+7 of the tile for all 64 queries;
-//   softmax -- the tile's row max comes from the waves' partial maxima, and
-//              wave w turns its own 8 logits into weights;
-//   PV      -- wave w accumulates head-dim entries 8w .. 8w+7 of the output
-//              over all 64 keys.
-// K and V are staged in LDS as fp64 (converted once, on load).  Logits are
-// accumulated in fp64: at this shape's logit magnitudes (|s| of a few tens) a
-// plain fp32 dot product of 64 terms is off by a few 1e-5, more than an fp32
-// output can afford.  The exponent argument is formed in fp64 and rounded
-// once to fp32 for exp; sums and the output accumulator stay in fp64.  The
-// online softmax is folded once per tile; the QK-Skip test compares the
-// tile's maximum with the running max taken before it.  Plain VALU
-// arithmetic, not MFMA: the fp32 workloads are small and latency-bound.
+// One workgroup of 8 waves per (batch, head, q-tile).  Both contractions
+// run on the fp64 matrix cores (v_mfma_f64_16x16x4f64: 16x16 blocks, 4 terms
+// per step):
+//   logits  S^T = K Q^T -- wave w owns key block w/2 (16 keys) and query
+//           blocks 2(w%2), 2(w%2)+1, with Q^T in registers and K from LDS;
+//   softmax on the accumulators: the tile's row max from per-wave maxima
+//           (LDS), the weights into an LDS buffer P[key][query];
+//   PV      O^T = V^T P^T -- wave w owns head-dim block w/2 for the same two
+//           query blocks, so a lane's online-softmax state (two queries) is
+//           the same in both phases.
+// Matrix-core operands: lane l holds A[l%16][l/16] and B[l/16][l%16] of each
+// 16x4 / 4x16 step, and D[l/16 + 4r][l%16], r = 0..3, of the 16x16 result.
+// K (transposed), V and P sit in LDS as fp64 with a row stride of 80
+// doubles, so each 32-lane half of an operand read touches distinct banks.
+// The next tile's K and V are loaded into registers a whole tile ahead.
+// Arithmetic: fp64 logits (at this shape's logit magnitudes, |s| of a few
+// tens, a plain fp32 dot product of 64 terms is off by a few 1e-5, more than
+// an fp32 output can afford); the exponent argument formed in fp64 and
+// rounded once to fp32 for exp; sums and the output accumulator in fp64.
+// The online softmax is folded once per tile; the QK-Skip test compares the
+// tile's maximum with the running max taken before it.
 #include "lite_attn_internal.h"
 
 #include <math.h>
@@ -29,18 +35,26 @@ constexpr int TILE = 64;  // BM = BN = 64
 constexpr int DIM = 64;
 constexpr int MAXW = 128;
 constexpr int NWAVE = 8;
-constexpr int KPW = TILE / NWAVE;  // keys (logits) and head-dim entries (PV) per wave
+constexpr int LD = 80;  // LDS row stride (doubles) of Kt, Vd and P
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ double xor_max(double x, int m) { return fmax(x, __shfl_xor(x, m)); }
+__device__ __forceinline__ double xor_sum(double x, int m) { return x + __shfl_xor(x, m); }
 
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512))) fwd_fp32_kernel(FwdParams p)
 {
-    __shared__ double Kd[TILE][DIM];
-    __shared__ double Vd[TILE][DIM];
-    __shared__ double S[TILE][TILE];   // [key][query]: logits, then weights
-    __shared__ double mx[NWAVE][TILE]; // per-wave maximum over its keys, per query
-    __shared__ double ps[NWAVE][TILE]; // per-wave sum of its weights, per query
+    __shared__ double Kt[DIM][LD];   // K transposed: [head-dim][key]
+    __shared__ double Vd[TILE][LD];  // [key][head-dim]
+    __shared__ double P[TILE][LD];   // [key][query]: the tile's weights
+    __shared__ double mx[4][TILE];   // per key block: maximum logit, per query
+    __shared__ double ps[4][TILE];   // per key block: sum of weights, per query
     __shared__ uint32_t keep[MAXW];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int xb = wv >> 1;             // key block (logits) / head-dim block (PV)
+    const int qb0 = 2 * (wv & 1);       // first of this wave's two query blocks
     const int Nq = p.Nq, Nk = p.Nk, H = p.H, Tq = p.Tq, Tk = p.Tk, W = p.W;
     const int64_t row = blockIdx.x;
     const int qt = (int)(row % Tq);
@@ -63,26 +77,26 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512))) fwd_fp32_
     for (int w = tid; w < W; w += 512)
         keep[w] = ranges ? p.rg.skip_bits[w] : 0u;
 
-    // this lane's query, in fp64
-    const int qi = qt * TILE + lane;
-    const bool qvalid = qi < Nq;
-    double qd[DIM];
+    // this lane's two queries (one per query block) and their Q^T operands:
+    // step s of block j takes Q[query_j][4s + g]
+    int qi[2];
+    bool qv[2];
+    double qf[2][DIM / 4];
 #pragma unroll
-    for (int e = 0; e < DIM; e += 4) {
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (qvalid)
-            x = *(const float4 *)(Qb + (int64_t)qi * rs + e);
-        qd[e] = x.x;
-        qd[e + 1] = x.y;
-        qd[e + 2] = x.z;
-        qd[e + 3] = x.w;
+    for (int j = 0; j < 2; ++j) {
+        qi[j] = qt * TILE + (qb0 + j) * 16 + l16;
+        qv[j] = qi[j] < Nq;
+        const float *qr = Qb + (int64_t)qi[j] * rs + g;
+#pragma unroll
+        for (int st = 0; st < DIM / 4; ++st)
+            qf[j][st] = qv[j] ? (double)qr[4 * st] : 0.0;
     }
 
-    double o[KPW];  // head-dim entries wv*KPW .. +KPW of this lane's output
+    f64x4 O[2];  // O^T block (head-dim block xb, query block qb0 + j)
 #pragma unroll
-    for (int e = 0; e < KPW; ++e)
-        o[e] = 0.0;
-    double m_run = -INFINITY, l_run = 0.0;  // identical in every wave
+    for (int j = 0; j < 2; ++j)
+        O[j] = (f64x4){0.0, 0.0, 0.0, 0.0};
+    double m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0, 0.0};
 
     // live k-tiles in visiting order (descending): Skip-List or mask words
     // (must-do tiles live whatever the mask says, must-skip tiles never).
@@ -103,154 +117,156 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512))) fwd_fp32_
     } else if (W > 0) {
         cur = live_word(wi);
     }
-
-    // K/V tile staging: thread tid converts 8 consecutive elements of key
-    // row tid / 8 (columns (tid % 8) * 8 ..) of each
-    const int lc = tid >> 3, le = (tid & 7) * 8;
-
-    for (;;) {
-        int kt = -1;
+    auto next_tile = [&]() -> int {
         if (list) {
             if (idx < cnt) {
-                kt = list[1 + idx++];
-                if (kt < 0 || kt >= Tk)
-                    kt = -1;
+                const int kt = list[1 + idx++];
+                return (kt < 0 || kt >= Tk) ? -1 : kt;
             }
-        } else {
-            while (cur == 0 && wi > 0) {
-                --wi;
-                cur = live_word(wi);
-            }
-            if (cur != 0) {
-                const int bit = 31 - __builtin_clz(cur);
-                cur &= ~(1u << bit);
-                kt = wi * 32 + bit;
-            }
+            return -1;
         }
-        if (kt < 0)
-            break;
-        const int key0 = kt * TILE;
+        while (cur == 0 && wi > 0) {
+            --wi;
+            cur = live_word(wi);
+        }
+        if (cur == 0)
+            return -1;
+        const int bit = 31 - __builtin_clz(cur);
+        cur &= ~(1u << bit);
+        return wi * 32 + bit;
+    };
 
+    // K/V staging: thread tid holds 8 consecutive elements (head-dim (tid % 8) * 8 ..)
+    // of key row tid / 8 of the next tile, loaded a tile ahead
+    const int lc = tid >> 3, le = (tid & 7) * 8;
+    float4 pk0, pk1, pv0, pv1;
+    auto fetch = [&](int kt) {
+        const int key = kt * TILE + lc;
+        pk0 = pk1 = pv0 = pv1 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (kt >= 0 && key < Nk) {
+            const float *kr = Kb + (int64_t)key * rs + le;
+            const float *vr = Vb + (int64_t)key * rs + le;
+            pk0 = *(const float4 *)kr;
+            pk1 = *(const float4 *)(kr + 4);
+            pv0 = *(const float4 *)vr;
+            pv1 = *(const float4 *)(vr + 4);
+        }
+    };
+
+    int kt = next_tile();
+    fetch(kt);
+    while (kt >= 0) {
+        const int key0 = kt * TILE;
         __syncthreads();  // the previous tile is fully consumed
         {
-            const int key = key0 + lc;
-            float4 k0 = make_float4(0.f, 0.f, 0.f, 0.f), k1 = k0, v0 = k0, v1 = k0;
-            if (key < Nk) {
-                const float *kr = Kb + (int64_t)key * rs + le;
-                const float *vr = Vb + (int64_t)key * rs + le;
-                k0 = *(const float4 *)kr;
-                k1 = *(const float4 *)(kr + 4);
-                v0 = *(const float4 *)vr;
-                v1 = *(const float4 *)(vr + 4);
-            }
-            double *kd = &Kd[lc][le];
+            const float kx[8] = {pk0.x, pk0.y, pk0.z, pk0.w, pk1.x, pk1.y, pk1.z, pk1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                Kt[le + e][lc] = kx[e];
             double *vd = &Vd[lc][le];
-            *(double2 *)(kd + 0) = make_double2(k0.x, k0.y);
-            *(double2 *)(kd + 2) = make_double2(k0.z, k0.w);
-            *(double2 *)(kd + 4) = make_double2(k1.x, k1.y);
-            *(double2 *)(kd + 6) = make_double2(k1.z, k1.w);
-            *(double2 *)(vd + 0) = make_double2(v0.x, v0.y);
-            *(double2 *)(vd + 2) = make_double2(v0.z, v0.w);
-            *(double2 *)(vd + 4) = make_double2(v1.x, v1.y);
-            *(double2 *)(vd + 6) = make_double2(v1.z, v1.w);
+            *(double2 *)(vd + 0) = make_double2(pv0.x, pv0.y);
+            *(double2 *)(vd + 2) = make_double2(pv0.z, pv0.w);
+            *(double2 *)(vd + 4) = make_double2(pv1.x, pv1.y);
+            *(double2 *)(vd + 6) = make_double2(pv1.z, pv1.w);
         }
+        const int kt_next = next_tile();
+        fetch(kt_next);
         __syncthreads();
 
-        // logits of this wave's keys (fp64 dot products in head-dim order)
-        {
-            double s[KPW];
+        // logits S^T of key block xb for this wave's two query blocks
+        f64x4 Sacc[2] = {(f64x4){0.0, 0.0, 0.0, 0.0}, (f64x4){0.0, 0.0, 0.0, 0.0}};
 #pragma unroll
-            for (int j = 0; j < KPW; ++j)
-                s[j] = 0.0;
+        for (int st = 0; st < DIM / 4; ++st) {
+            const double a = Kt[4 * st + g][xb * 16 + l16];
 #pragma unroll
-            for (int e = 0; e < DIM; e += 2) {
+            for (int j = 0; j < 2; ++j)
+                Sacc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, qf[j][st], Sacc[j], 0, 0, 0);
+        }
+        // lane holds keys xb*16 + g + 4r of query qi[j]
+        double sv[2][4];
+        double wmax[2];
 #pragma unroll
-                for (int j = 0; j < KPW; ++j) {
-                    const double2 kk = *(const double2 *)&Kd[wv * KPW + j][e];
-                    s[j] = fma(qd[e], kk.x, s[j]);
-                    s[j] = fma(qd[e + 1], kk.y, s[j]);
-                }
-            }
+        for (int j = 0; j < 2; ++j) {
             double m = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < KPW; ++j) {
-                const double sj = (key0 + wv * KPW + j < Nk) ? s[j] * scale : -INFINITY;
-                S[wv * KPW + j][lane] = sj;
-                m = fmax(m, sj);
+            for (int r = 0; r < 4; ++r) {
+                const int key = key0 + xb * 16 + g + 4 * r;
+                sv[j][r] = key < Nk ? Sacc[j][r] * scale : -INFINITY;
+                m = fmax(m, sv[j][r]);
             }
-            mx[wv][lane] = m;
+            m = xor_max(m, 16);
+            m = xor_max(m, 32);
+            wmax[j] = m;
+        }
+        if (g == 0) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                mx[xb][(qb0 + j) * 16 + l16] = wmax[j];
         }
         __syncthreads();
 
         // the tile's row max, the online-softmax update, this wave's weights
-        double m_tile = mx[0][lane];
+        double alpha[2];
+        bool keep_lane = false;
 #pragma unroll
-        for (int w = 1; w < NWAVE; ++w)
-            m_tile = fmax(m_tile, mx[w][lane]);
-        const double m_before = m_run;
-        const double m_new = fmax(m_run, m_tile);
-        const bool upd = m_new > -INFINITY;
-        const double alpha = upd ? exp(m_run - m_new) : 1.0;
-        {
+        for (int j = 0; j < 2; ++j) {
+            const int qc = (qb0 + j) * 16 + l16;
+            const double m_tile = fmax(fmax(mx[0][qc], mx[1][qc]), fmax(mx[2][qc], mx[3][qc]));
+            const double m_before = m_run[j];
+            const double m_new = fmax(m_run[j], m_tile);
+            const bool upd = m_new > -INFINITY;
+            alpha[j] = upd ? exp(m_run[j] - m_new) : 1.0;
             double sum = 0.0;
 #pragma unroll
-            for (int j = 0; j < KPW; ++j) {
-                const double pj = upd ? (double)expf((float)(S[wv * KPW + j][lane] - m_new)) : 0.0;
-                S[wv * KPW + j][lane] = pj;
+            for (int r = 0; r < 4; ++r) {
+                const double pj = upd ? (double)expf((float)(sv[j][r] - m_new)) : 0.0;
+                P[xb * 16 + g + 4 * r][qc] = pj;
                 sum += pj;
             }
-            ps[wv][lane] = sum;
+            sum = xor_sum(sum, 16);
+            sum = xor_sum(sum, 32);
+            if (g == 0)
+                ps[xb][qc] = sum;
+            m_run[j] = m_new;
+            keep_lane = keep_lane || (qv[j] && !(m_tile - m_before < tau));
         }
-        m_run = m_new;
-        if (vote && wv == 0) {
+        if (vote && xb == 0) {
             // a must-do tile is never marked
             const bool must_do = ranges && ((p.rg.do_bits[kt >> 5] >> (kt & 31)) & 1u);
-            const bool keep_lane = must_do || (qvalid && !(m_tile - m_before < tau));
-            if (__ballot(keep_lane) != 0ull && lane == 0)
-                keep[kt >> 5] |= 1u << (kt & 31);
+            if (__ballot(keep_lane || must_do) != 0ull && lane == 0)
+                atomicOr(&keep[kt >> 5], 1u << (kt & 31));
         }
         __syncthreads();
 
-        // row sum and this wave's slice of the output
-        {
-            double tsum = 0.0;
+        // row sums, and this wave's block of the output: O^T += V^T P^T
 #pragma unroll
-            for (int w = 0; w < NWAVE; ++w)
-                tsum += ps[w][lane];
-            l_run = l_run * alpha + tsum;
-#pragma unroll
-            for (int e = 0; e < KPW; ++e)
-                o[e] *= alpha;
-#pragma unroll 8
-            for (int c = 0; c < TILE; ++c) {
-                const double pc = S[c][lane];
-                const double *vr = &Vd[c][wv * KPW];
-#pragma unroll
-                for (int e = 0; e < KPW; e += 2) {
-                    const double2 vv = *(const double2 *)(vr + e);
-                    o[e] = fma(pc, vv.x, o[e]);
-                    o[e + 1] = fma(pc, vv.y, o[e + 1]);
-                }
-            }
+        for (int j = 0; j < 2; ++j) {
+            const int qc = (qb0 + j) * 16 + l16;
+            l_run[j] = l_run[j] * alpha[j] + (((ps[0][qc] + ps[1][qc]) + ps[2][qc]) + ps[3][qc]);
+            O[j] *= alpha[j];
         }
+#pragma unroll
+        for (int st = 0; st < TILE / 4; ++st) {
+            const double a = Vd[4 * st + g][xb * 16 + l16];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                O[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, P[4 * st + g][(qb0 + j) * 16 + l16], O[j], 0, 0, 0);
+        }
+        kt = kt_next;
     }
 
-    if (qvalid) {
-        float *Ob = (float *)p.out + (int64_t)b * p.o_sb + (int64_t)h * DIM + (int64_t)qi * rs + wv * KPW;
-        const double inv = l_run > 0.0 ? 1.0 / l_run : 0.0;
-        float4 r0, r1;
-        r0.x = (float)(o[0] * inv);
-        r0.y = (float)(o[1] * inv);
-        r0.z = (float)(o[2] * inv);
-        r0.w = (float)(o[3] * inv);
-        r1.x = (float)(o[4] * inv);
-        r1.y = (float)(o[5] * inv);
-        r1.z = (float)(o[6] * inv);
-        r1.w = (float)(o[7] * inv);
-        *(float4 *)Ob = r0;
-        *(float4 *)(Ob + 4) = r1;
-        if (p.lse && wv == 0)
-            p.lse[bh * Nq + qi] = l_run > 0.0 ? (float)(m_run + log(l_run)) : -INFINITY;
+    // lane holds head-dim entries xb*16 + g + 4r of queries qi[0], qi[1]
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if (!qv[j])
+            continue;
+        float *Ob = (float *)p.out + (int64_t)b * p.o_sb + (int64_t)h * DIM + (int64_t)qi[j] * rs + xb * 16 + g;
+        const double inv = l_run[j] > 0.0 ? 1.0 / l_run[j] : 0.0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Ob[4 * r] = (float)(O[j][r] * inv);
+        if (p.lse && xb == 0 && g == 0)
+            p.lse[bh * Nq + qi[j]] = l_run[j] > 0.0 ? (float)(m_run[j] + log(l_run[j])) : -INFINITY;
     }
     if (vote) {
         __syncthreads();
