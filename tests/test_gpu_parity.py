@@ -182,6 +182,22 @@ def test_maximum_k_tiles():
     pa.compare_rows(gpu, orc, rows, 1, N, H, 128, 128, -3.0, torch.bfloat16)
 
 
+@pytest.mark.parametrize("N,density,skiplist", [(4096 * 64 - 17, 0.95, False), (4096 * 64 - 17, 0.95, True),
+                                                (20000, 0.5, False), (20000, 0.5, True)])
+def test_fp32_long_sequences_sampled_rows(N, density, skiplist):
+    """The fp32 kernel over many k-tiles: up to Tk = 4096 (128 mask words per
+    row), ragged last tile, bitmask and Skip-List paths, on sampled rows."""
+    H, D, T = 1, 64, 64
+    Tq = Tk = -(-N // T)
+    log("  fp32 N %d Tk %d density %.2f skiplist %s" % (N, Tk, density, skiplist))
+    q, k, v = synth.random_qkv(1, N, H, D, torch.float32, seed=3, scale=1.5, device="cuda")
+    mask = synth.random_mask(H * Tq, Tk, density, seed=12).numpy()
+    rows = np.array([0, Tq // 3, Tq - 1], np.int64)
+    gpu = pa.gpu_fwd(q, k, v, T, T, -3.0, 0.125, mask_in=mask, use_skiplist=skiplist)
+    orc = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), T, T, -3.0, 0.125, mask_in=mask, rows=rows)
+    log("  ", pa.compare_rows(gpu, orc, rows, 1, N, H, T, T, -3.0, torch.float32))
+
+
 @pytest.mark.parametrize("name", ["c3_bf16_33k", "c4_bf16_76k", "c5_bf16_76k_pair"])
 def test_full_size_sampled_rows(name):
     """Full-size workloads in the benchmark's launch configuration: step 0 (empty
