@@ -89,13 +89,20 @@ def pair_occupancy(mask_words, wl):
     return float((a.sum() + b.sum()) / (2.0 * union)) if union > 0 else 1.0
 
 
-def aux_kernels(mask_words, wl, sl_ms, reset_ms):
-    """HBM roofline of the two mask kernels, from algorithmic bytes and the
+def hbm_entry(b, ms):
+    return {"bound": "hbm", "us": round(ms * 1e3, 2), "bytes": b, "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+            "frac": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def aux_kernels(mask_words, wl, sl_ms, reset_ms, merge_ms, err_ms):
+    """HBM roofline of the other kernels, from algorithmic bytes and the
     HIP-event time of one call (mean of 10 back-to-back calls).
 
     Skip-List build: every mask word read once, and per row the count plus
     one entry per live tile written (4 bytes each).  Mask reset: every mask
-    word written once."""
+    word written once.  LSE merge of 2 parts: per (query, head) both parts'
+    d outputs and lse read, the merged ones written.  Error sums: both
+    tensors read once."""
     import torch
     w = mask_words.view(wl.rows, wl.mask_words).to(torch.int64) & 0xFFFFFFFF
     bits = (w[:, :, None] >> torch.arange(32, device=w.device)) & 1
@@ -103,14 +110,12 @@ def aux_kernels(mask_words, wl, sl_ms, reset_ms):
     words = w.numel()
     out = {}
     if sl_ms is not None:
-        b = 4 * words + 4 * int((1 + wl.tk - marked).sum())
-        out["skiplist_build"] = {"bound": "hbm", "us": round(sl_ms * 1e3, 2), "bytes": b,
-                                 "GB/s": round(b / (sl_ms * 1e-3) / 1e9, 1),
-                                 "frac": round(b / (sl_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    b = 4 * words
-    out["reset_mask"] = {"bound": "hbm", "us": round(reset_ms * 1e3, 2), "bytes": b,
-                         "GB/s": round(b / (reset_ms * 1e-3) / 1e9, 1),
-                         "frac": round(b / (reset_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        out["skiplist_build"] = hbm_entry(4 * words + 4 * int((1 + wl.tk - marked).sum()), sl_ms)
+    out["reset_mask"] = hbm_entry(4 * words, reset_ms)
+    qh = wl.batch * wl.seqlen * wl.heads
+    row_bytes = wl.head_dim * 2 + 4                                      # bf16 output row + fp32 lse
+    out["lse_merge_2_parts"] = hbm_entry(3 * qh * row_bytes, merge_ms)
+    out["error_sums"] = hbm_entry(2 * qh * wl.head_dim * 2, err_ms)
     return out
 
 
@@ -267,11 +272,27 @@ def main():
     for _ in range(10):
         la.lite_attn_reset_mask(desc, warm_mask[0])
     aux_ev[1][1].record()
+    # LSE merge of two partial attentions and the calibration's error sums, at
+    # this workload's shape (the forward's output as the data, lse 0)
+    out_b, out_m = out.clone(), torch.empty_like(out)
+    lses = [torch.zeros(wl.batch, wl.heads, wl.seqlen, dtype=torch.float32, device=dev) for _ in range(3)]
+    sums = torch.empty(2, dtype=torch.float64, device=dev)
+    aux_ev += [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2)]
+    aux_ev[2][0].record()
+    for _ in range(10):
+        la.lite_attn_merge([out, out_b], lses[:2], out_m, lses[2])
+    aux_ev[2][1].record()
+    aux_ev[3][0].record()
+    for _ in range(10):
+        la.lite_attn_error_sums(out_m, out, sums)
+    aux_ev[3][1].record()
     torch.cuda.synchronize()
     dense_ms = [a.elapsed_time(b) for a, b in dev_ms]
     sl_ms = aux_ev[0][0].elapsed_time(aux_ev[0][1]) / 10 if sl is not None else None
     reset_ms = aux_ev[1][0].elapsed_time(aux_ev[1][1]) / 10
-    aux = aux_kernels(masks[K], wl, sl_ms, reset_ms)
+    aux = aux_kernels(masks[K], wl, sl_ms, reset_ms, aux_ev[2][0].elapsed_time(aux_ev[2][1]) / 10,
+                      aux_ev[3][0].elapsed_time(aux_ev[3][1]) / 10)
+    del out_b, out_m, lses
     del inputs
 
     value = sum(flops) / wall / 1e12

@@ -2,9 +2,11 @@
 // Calibration": error budgets per timestep, stricter early): the sums behind
 // a relative output error, ||a - b||^2 and ||b||^2, in fp64.
 //
-// HBM-bound: each element of a and b is read once.  One thread per 8
-// consecutive head-dim elements of one (b, n, h), grid-stride; each wave adds
-// its partial sums into the two doubles with one atomic each.
+// HBM-bound: each element of a and b is read once.  Within one batch entry
+// the (n, h, d) elements of a BSHD tensor are contiguous, so the kernel walks
+// the batch entries in turn and, within one, takes 8 consecutive elements per
+// thread, grid-stride, at offset 8t: no index arithmetic beyond that.  Each
+// block adds its partial sums into the two doubles with one atomic each.
 #include "lite_attn_internal.h"
 
 namespace lite_attn {
@@ -41,24 +43,36 @@ __global__ void __launch_bounds__(256) zero2_kernel(double *sums)
 
 __global__ void __launch_bounds__(256) error_sums_kernel(ErrParams p)
 {
-    const int cpq = p.D / 8;
-    const int64_t total = (int64_t)p.B * p.N * p.H * cpq;
+    const int64_t per_b = (int64_t)p.N * p.H * (p.D / 8);  // 8-element chunks per batch entry
+    const int64_t stride = (int64_t)gridDim.x * 256;
     double s0 = 0.0, s1 = 0.0;
-    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256) {
-        const int c = (int)(t % cpq);
-        const int64_t qid = t / cpq;  // (b, n, h) in BSHD order
-        const int h = (int)(qid % p.H);
-        const int64_t bn = qid / p.H;
-        const int n = (int)(bn % p.N), b = (int)(bn / p.N);
-        const int64_t inner = ((int64_t)n * p.H + h) * p.D + 8 * c;
-        float x[8], y[8];
-        load8(p.a, (int64_t)b * p.a_sb + inner, p.dtype, x);
-        load8(p.b, (int64_t)b * p.b_sb + inner, p.dtype, y);
+    for (int b = 0; b < p.B; ++b) {
+        const int64_t ab = (int64_t)b * p.a_sb, bb = (int64_t)b * p.b_sb;
+        // four chunks per pass, all loads issued before any arithmetic, so
+        // that enough bytes are in flight to cover the memory latency; chunks
+        // past the end are zeros and add nothing
+        for (int64_t t0 = (int64_t)blockIdx.x * 256 + threadIdx.x; t0 < per_b; t0 += 4 * stride) {
+            float x[4][8], y[4][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const double d = (double)x[j] - (double)y[j];
-            s0 = fma(d, d, s0);
-            s1 = fma((double)y[j], (double)y[j], s1);
+            for (int u = 0; u < 4; ++u) {
+                const int64_t t = t0 + u * stride;
+                if (t < per_b) {
+                    load8(p.a, ab + 8 * t, p.dtype, x[u]);
+                    load8(p.b, bb + 8 * t, p.dtype, y[u]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        x[u][j] = y[u][j] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const double d = (double)x[u][j] - (double)y[u][j];
+                    s0 = fma(d, d, s0);
+                    s1 = fma((double)y[u][j], (double)y[u][j], s1);
+                }
         }
     }
 #pragma unroll
@@ -66,9 +80,17 @@ __global__ void __launch_bounds__(256) error_sums_kernel(ErrParams p)
         s0 += __shfl_xor(s0, off);
         s1 += __shfl_xor(s1, off);
     }
+    // the block's four waves meet in LDS: one atomic pair per block, since
+    // atomics on the same two addresses serialise
+    __shared__ double part[2][4];
     if ((threadIdx.x & 63) == 0) {
-        atomicAdd(&p.sums[0], s0);
-        atomicAdd(&p.sums[1], s1);
+        part[0][threadIdx.x >> 6] = s0;
+        part[1][threadIdx.x >> 6] = s1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        atomicAdd(&p.sums[0], (part[0][0] + part[0][1]) + (part[0][2] + part[0][3]));
+        atomicAdd(&p.sums[1], (part[1][0] + part[1][1]) + (part[1][2] + part[1][3]));
     }
 }
 
@@ -83,8 +105,8 @@ hipError_t launch_error_sums(const ErrParams &p, hipStream_t stream)
     if (total <= 0)
         return hipGetLastError();
     int64_t blocks = (total + 255) / 256;
-    if (blocks > 4096)
-        blocks = 4096;
+    if (blocks > 1024)
+        blocks = 1024;  // four per CU: enough loads in flight, few atomics
     hipLaunchKernelGGL(error_sums_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
