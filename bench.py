@@ -19,6 +19,13 @@ Printed (one JSON line on stdout):
   tau_sweep        per-threshold trajectories (-inf, -10, -3, 0): sparsity,
                    kernel time, speedup and a least-squares fit of t/t_dense
                    against the live fraction
+  aux_kernels      HBM roofline of the Skip-List build, the mask reset, the
+                   LSE merge and the error sums at the workload's shape
+  dense_variants   with --dense-variants: every bf16 kernel instantiation
+                   (head_dim, key-tile width) dense at 32,768 tokens x 32 heads
+
+--workload c1_fp32_1k measures the fp32 path instead (fp64 arithmetic on the
+fp64 matrix cores, against their 78.6 TFLOP/s peak).
 """
 
 import argparse
@@ -34,19 +41,21 @@ sys.path.insert(0, ROOT)
 
 METRIC = "effective TFLOP/s on live tiles + % MFMA peak + speedup vs dense, 75.6k-token DiT"
 PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP64_TFLOPS = 78.6   # fp64 matrix (and vector) peak: the fp32 path computes in fp64
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_c4_76k.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "temporal_block_sparse_amd", "csrc", f)
-                  for f in ("fwd_bf16.hip", "lite_attn_internal.h")]
+KERNEL_SOURCES = {dt: [os.path.join(ROOT, "temporal_block_sparse_amd", "csrc", f)
+                      for f in (src, "lite_attn_internal.h")]
+                  for dt, src in (("bf16", "fwd_bf16.hip"), ("fp32", "fwd_fp32.hip"))}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+def kernel_source_hash(dtype="bf16"):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[dtype]:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -113,10 +122,37 @@ def aux_kernels(mask_words, wl, sl_ms, reset_ms, merge_ms, err_ms):
         out["skiplist_build"] = hbm_entry(4 * words + 4 * int((1 + wl.tk - marked).sum()), sl_ms)
     out["reset_mask"] = hbm_entry(4 * words, reset_ms)
     qh = wl.batch * wl.seqlen * wl.heads
-    row_bytes = wl.head_dim * 2 + 4                                      # bf16 output row + fp32 lse
+    esz = 2 if wl.dtype == "bf16" else 4
+    row_bytes = wl.head_dim * esz + 4                                    # output row + fp32 lse
     out["lse_merge_2_parts"] = hbm_entry(3 * qh * row_bytes, merge_ms)
-    out["error_sums"] = hbm_entry(2 * qh * wl.head_dim * 2, err_ms)
+    out["error_sums"] = hbm_entry(2 * qh * wl.head_dim * esz, err_ms)
     return out
+
+
+def dense_variants(torch, la, N=32768, H=32):
+    """Dense throughput of each bf16 kernel instantiation (head_dim, key-tile
+    width) at one large shape: seeded N(0,1) q, k, v, no mask, tau = -inf;
+    5 back-to-back launches after 2 warmups, timed with events."""
+    res = []
+    for D, BN in ((64, 64), (64, 128), (128, 64), (128, 128)):
+        g = torch.Generator(device="cuda").manual_seed(0)
+        q, k, v = (torch.randn(1, N, H, D, device="cuda", generator=g).to(torch.bfloat16) for _ in range(3))
+        o = torch.empty_like(q)
+        sc = 1.0 / math.sqrt(D)
+        for _ in range(2):
+            la.lite_attn_fwd(q, k, v, o, tile_m=128, tile_n=BN, tau=-math.inf, softmax_scale=sc)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            la.lite_attn_fwd(q, k, v, o, tile_m=128, tile_n=BN, tau=-math.inf, softmax_scale=sc)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        res.append({"head_dim": D, "tile": "128x%d" % BN, "seq_len": N, "heads": H, "ms": round(ms, 3),
+                    "tflops": round(4.0 * H * N * N * D / (ms * 1e-3) / 1e12, 1)})
+        log("[bench] dense d=%d tile 128x%d: %.3f ms" % (D, BN, ms))
+        del q, k, v, o
+    return res
 
 
 def read_traffic(src_hash):
@@ -161,11 +197,16 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4_bf16_76k")
+    ap.add_argument("--grid", default=None, help="F,H,W token grid overriding the workload's (same recipe)")
+    ap.add_argument("--heads", type=int, default=None, help="head count overriding the workload's")
     ap.add_argument("--tau", type=float, default=-3.0)
     ap.add_argument("--path", choices=("skiplist", "bitmask"), default="skiplist")
     ap.add_argument("--sweep-steps", type=int, default=50, help="steps of the tau sweep (0: skip)")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle rows for the CPU baseline (0: 2 per thread)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--dense-variants", action="store_true",
+                    help="also time every bf16 kernel instantiation (head_dim, key-tile width) dense at 32,768 "
+                         "tokens x 32 heads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -189,8 +230,12 @@ def main():
     from temporal_block_sparse_amd import lite_attn as la
 
     wl = configs.ALL[args.workload]
-    if wl.dtype != "bf16":
-        sys.exit("bench.py measures the bf16 path")
+    if args.grid or args.heads:
+        grid = tuple(int(x) for x in args.grid.split(",")) if args.grid else wl.grid
+        wl = configs.scaled(wl, grid, heads=args.heads, name="%s_grid%s_h%d" % (
+            wl.name, "x".join(str(x) for x in grid), args.heads or wl.heads))
+    bf16 = wl.dtype == "bf16"   # else the fp32 path (fp64 arithmetic on the fp64 matrix cores)
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP64_TFLOPS
     dev = torch.device("cuda")
     scale = 1.0 / math.sqrt(wl.head_dim)
     K, W = args.steps, args.warmup
@@ -198,12 +243,14 @@ def main():
         % (wl.name, wl.batch, wl.heads, wl.seqlen, wl.head_dim, wl.tile_m, wl.tile_n, args.tau, args.path, W, K))
 
     tr = synth.Trajectory(wl, dev)
-    desc = la.make_desc(wl.batch, wl.seqlen, wl.heads, wl.head_dim, wl.tile_m, wl.tile_n, la.LITE_BF16)
+    desc = la.make_desc(wl.batch, wl.seqlen, wl.heads, wl.head_dim, wl.tile_m, wl.tile_n,
+                        la.LITE_BF16 if bf16 else la.LITE_FP32)
     nw = la.lite_attn_mask_words(desc)
     masks = [torch.zeros(nw, dtype=torch.int32, device=dev) for _ in range(K + 1)]
     warm_mask = [torch.zeros(nw, dtype=torch.int32, device=dev), torch.zeros(nw, dtype=torch.int32, device=dev)]
     sl = la.alloc_skiplist(desc, dev) if args.path == "skiplist" else None
-    out = torch.empty(wl.batch, wl.seqlen, wl.heads, wl.head_dim, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(wl.batch, wl.seqlen, wl.heads, wl.head_dim, dtype=torch.bfloat16 if bf16 else torch.float32,
+                      device=dev)
 
     def step(q, k, v, m_in, m_out, tau, ev=None):
         if sl is not None:
@@ -297,8 +344,11 @@ def main():
 
     value = sum(flops) / wall / 1e12
     achieved = sum(flops) / (sum(kern_ms) * 1e-3) / 1e12
-    src_hash = kernel_source_hash()
-    traffic, traffic_note = read_traffic(src_hash)
+    src_hash = kernel_source_hash(wl.dtype)
+    if bf16 and wl.name == "c4_bf16_76k":
+        traffic, traffic_note = read_traffic(src_hash)
+    else:
+        traffic, traffic_note = None, "the committed counter summary covers the 75,600-token bf16 workload only"
     sparsity = [1.0 - f / dense_flops for f in flops]
     occupancy = [pair_occupancy(masks[t], wl) for t in range(K)]
 
@@ -390,14 +440,16 @@ def main():
                          "of %s" % (len(rows), wl.rows, tc, res["nthreads"], cpu_model())}
         del qc, kc, vc
 
+    variants = dense_variants(torch, la) if args.dense_variants else None
+
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(wall * 1e3 / K, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": "bf16" if bf16 else "fp64", "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "seq_len": wl.seqlen,
                    "grid": list(wl.grid), "head_dim": wl.head_dim, "tile": "%dx%d" % (wl.tile_m, wl.tile_n),
                    "tau": args.tau, "path": args.path, "timed_steps": [W, W + K - 1]},
-        "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "pct_mfma_peak": round(100.0 * value / peak, 2),
         "speedup_vs_dense": round(sum(dense_ms) / sum(kern_ms), 3),
         "dense_kernel_ms": round(sum(dense_ms) / K, 3), "kernel_ms": round(sum(kern_ms) / K, 3),
         "dense_tflops": round(dense_flops * K / (sum(dense_ms) * 1e-3) / 1e12, 1),
@@ -405,14 +457,16 @@ def main():
         "pair_occupancy": [round(o, 4) for o in occupancy],
         "skiplist_build_ms": round(sl_ms, 4) if sl_ms is not None else None,
         "aux_kernels": aux,
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4),
                      "traffic": traffic, "traffic_note": traffic_note,
-                     "kernel": "fwd_bf16_kernel<%d, %d, %s>" % (wl.head_dim, wl.tile_n,
-                                                                 "true" if args.path == "skiplist" else "false"),
+                     "kernel": ("fwd_bf16_kernel<%d, %d, %s>" % (wl.head_dim, wl.tile_n,
+                                                                  "true" if args.path == "skiplist" else "false"))
+                     if bf16 else "fwd_fp32_kernel",
                      "kernel_source_sha256_16": src_hash},
         "cpu_baseline": cpu,
         "tau_sweep": sweep,
+        "dense_variants": variants,
     }
     print(json.dumps(res), flush=True)
 

@@ -90,7 +90,7 @@ ALL = {w.name: w for w in (C1, C2, C3, C4, C5)}
 
 
 def scaled(w: Workload, grid, heads=None, batch=None, steps=None, name=None):
-    """Same recipe on a smaller grid (for parity tests the oracle finishes quickly)."""
+    """Same recipe on another grid (the parity tests use smaller ones, which the oracle finishes quickly)."""
     kw = dict(w.__dict__)
     kw["grid"] = tuple(grid)
     if heads is not None:
