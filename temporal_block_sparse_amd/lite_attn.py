@@ -113,15 +113,34 @@ def lite_attn_skiplist_len(desc):
     return int(LIB.lite_attn_skiplist_len(ctypes.byref(desc)))
 
 
+def _on_device(t):
+    if t.numel() and not t.is_cuda:
+        raise ValueError("device tensor expected")
+    if t.is_cuda and t.device.index != torch.cuda.current_device():
+        raise ValueError("tensor on cuda:%d, but the current device is cuda:%d"
+                         % (t.device.index, torch.cuda.current_device()))
+
+
 def _ptr(t):
     """Device pointer of a contiguous tensor (masks, skip-lists, lse)."""
     if t is None:
         return None
-    if t.numel() and not t.is_cuda:
-        raise ValueError("device tensor expected")
+    _on_device(t)
     if not t.is_contiguous():
         raise ValueError("contiguous tensor expected")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _buf(t, nbytes, what, dtype=None):
+    """_ptr of a buffer the library reads or writes nbytes of: the kernels take
+    plain pointers, so a short tensor would be overrun -- refuse it here."""
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, not %s" % (what, dtype, t.dtype))
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s holds %d bytes; this call uses %d" % (what, t.numel() * t.element_size(), nbytes))
+    return _ptr(t)
 
 
 def _bshd(t):
@@ -130,8 +149,7 @@ def _bshd(t):
     along the sequence such as q[:, :text_len]."""
     if t.dim() != 4:
         raise ValueError("BSHD tensor expected")
-    if t.numel() and not t.is_cuda:
-        raise ValueError("device tensor expected")
+    _on_device(t)
     B, N, H, D = t.shape
     if N > 1 and t.stride(1) != H * D or H > 1 and t.stride(2) != D or D > 1 and t.stride(3) != 1:
         raise ValueError("each batch entry must be a contiguous [N][H][D] block")
@@ -191,21 +209,27 @@ def lite_attn_fwd(q, k, v, out, *, tile_m, tile_n, tau, softmax_scale=None, mask
     if _bshd(v)[4] != desc.kv_batch_stride:
         raise ValueError("v must be laid out like k")
     rg = _ranges(must_do, must_skip)
-    _check(LIB.lite_attn_fwd(ctypes.byref(desc), _bshd(q)[5], _bshd(k)[5], _bshd(v)[5], _ptr(mask_in),
-                             _ptr(mask_out), _ptr(skiplist), float(tau), float(softmax_scale), _bshd(out)[5],
-                             _ptr(lse), ctypes.byref(rg) if rg is not None else None, _stream(stream)))
+    mb = 4 * lite_attn_mask_words(desc)
+    _check(LIB.lite_attn_fwd(ctypes.byref(desc), _bshd(q)[5], _bshd(k)[5], _bshd(v)[5],
+                             _buf(mask_in, mb, "mask_in"), _buf(mask_out, mb, "mask_out"),
+                             _buf(skiplist, 4 * lite_attn_skiplist_len(desc), "skiplist"), float(tau),
+                             float(softmax_scale), _bshd(out)[5],
+                             _buf(lse, 4 * desc.batch * desc.heads * desc.seqlen, "lse", torch.float32),
+                             ctypes.byref(rg) if rg is not None else None, _stream(stream)))
     return out
 
 
 def lite_attn_build_skiplist(desc, mask, skiplist, must_do=None, must_skip=None, stream=None):
     rg = _ranges(must_do, must_skip)
-    _check(LIB.lite_attn_build_skiplist(ctypes.byref(desc), _ptr(mask), _ptr(skiplist),
+    _check(LIB.lite_attn_build_skiplist(ctypes.byref(desc), _buf(mask, 4 * lite_attn_mask_words(desc), "mask"),
+                                        _buf(skiplist, 4 * lite_attn_skiplist_len(desc), "skiplist"),
                                         ctypes.byref(rg) if rg is not None else None, _stream(stream)))
     return skiplist
 
 
 def lite_attn_reset_mask(desc, mask, stream=None):
-    _check(LIB.lite_attn_reset_mask(ctypes.byref(desc), _ptr(mask), _stream(stream)))
+    _check(LIB.lite_attn_reset_mask(ctypes.byref(desc), _buf(mask, 4 * lite_attn_mask_words(desc), "mask"),
+                                    _stream(stream)))
     return mask
 
 
@@ -223,8 +247,10 @@ def lite_attn_merge(outs, lses, out, lse=None, stream=None):
             raise ValueError("every part must match out's shape and share one layout")
     desc = make_desc(B, N, H, D, 1, 1, out.dtype, N, ps, ps, os_)
     po = (ctypes.c_void_p * n)(*[_bshd(o)[5] for o in outs])
-    pl = (ctypes.c_void_p * n)(*[_ptr(x) for x in lses])
-    _check(LIB.lite_attn_merge(ctypes.byref(desc), n, po, pl, optr, _ptr(lse), _stream(stream)))
+    lb = 4 * B * H * N
+    pl = (ctypes.c_void_p * n)(*[_buf(x, lb, "lses[%d]" % i, torch.float32) for i, x in enumerate(lses)])
+    _check(LIB.lite_attn_merge(ctypes.byref(desc), n, po, pl, optr, _buf(lse, lb, "lse", torch.float32),
+                               _stream(stream)))
     return out
 
 
@@ -238,7 +264,8 @@ def lite_attn_error_sums(a, b, sums=None, stream=None):
     if sums is None:
         sums = torch.empty(2, dtype=torch.float64, device=a.device)
     desc = make_desc(B, N, H, D, 1, 1, a.dtype, N, as_, 0, bs[4])
-    _check(LIB.lite_attn_error_sums(ctypes.byref(desc), ap, bs[5], _ptr(sums), _stream(stream)))
+    _check(LIB.lite_attn_error_sums(ctypes.byref(desc), ap, bs[5], _buf(sums, 16, "sums", torch.float64),
+                                    _stream(stream)))
     return sums
 
 

@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from temporal_block_sparse_amd import lite_attn as la
 
@@ -255,3 +256,19 @@ def test_error_sums_validation():
     assert f(ctypes.byref(desc(head_dim=12)), a, b, s, None) == 3
     assert f(ctypes.byref(desc(dtype=5)), a, b, s, None) == 3
     assert f(ctypes.byref(d), a, b, P(FAKE + 4096), None) == 7         # sums inside a
+
+
+def test_binding_refuses_short_mask_and_skiplist_buffers():
+    """The kernels take plain pointers; the binding checks every buffer holds
+    what the call will touch before anything is launched."""
+    d = la.make_desc(1, 1000, 2, 64, 128, 64, la.LITE_BF16)
+    nw, nl = la.lite_attn_mask_words(d), la.lite_attn_skiplist_len(d)
+    with pytest.raises(ValueError, match="mask holds"):
+        la.lite_attn_build_skiplist(d, torch.zeros(nw - 1, dtype=torch.int32), torch.zeros(nl, dtype=torch.int32))
+    with pytest.raises(ValueError, match="skiplist holds"):
+        la.lite_attn_build_skiplist(d, None, torch.zeros(nl - 1, dtype=torch.int32))   # no mask: nothing skipped
+    with pytest.raises(ValueError, match="mask holds"):
+        la.lite_attn_reset_mask(d, torch.zeros(nw - 1, dtype=torch.int32))
+    # right sizes, host memory: refused for the device
+    with pytest.raises(ValueError, match="device tensor expected"):
+        la.lite_attn_reset_mask(d, torch.zeros(nw, dtype=torch.int32))

@@ -219,3 +219,29 @@ def test_full_size_sampled_rows(name):
         st = pa.compare_rows(gpu, orc, rows, wl.batch, wl.seqlen, wl.heads, wl.tile_m, wl.tile_n, tau,
                              torch.bfloat16)
         log("  ", st)
+
+
+def test_binding_refuses_short_or_mistyped_buffers():
+    """The kernels take plain pointers: the binding refuses any buffer smaller
+    than the call uses (or of the wrong dtype) before launching anything."""
+    q, k, v = synth.random_qkv(1, 300, 2, 64, torch.bfloat16, seed=0, scale=1.0, device="cuda")
+    out = torch.empty_like(q)
+    desc = la.desc_of(q, 128, 64, k)
+    nw, nl = la.lite_attn_mask_words(desc), la.lite_attn_skiplist_len(desc)
+    m = torch.zeros(nw, dtype=torch.int32, device="cuda")
+    cases = ((dict(mask_in=m[:-1]), "mask_in holds"), (dict(mask_out=m[:-1]), "mask_out holds"),
+             (dict(mask_in=m, skiplist=torch.zeros(nl - 1, dtype=torch.int32, device="cuda")), "skiplist holds"),
+             (dict(lse=torch.zeros(1, 2, 299, device="cuda")), "lse holds"),
+             (dict(lse=torch.zeros(1, 2, 300, dtype=torch.float64, device="cuda")), "lse must be"))
+    for kw, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            la.lite_attn_fwd(q, k, v, out, tile_m=128, tile_n=64, tau=-3.0, **kw)
+    lse = torch.zeros(1, 2, 300, device="cuda")
+    with pytest.raises(ValueError, match=r"lses\[1\] holds"):
+        la.lite_attn_merge([out, out], [lse, torch.zeros(1, 2, 299, device="cuda")], torch.empty_like(out))
+    with pytest.raises(ValueError, match="sums must be"):
+        la.lite_attn_error_sums(out, out, torch.zeros(2, dtype=torch.float32, device="cuda"))
+    # the right buffers still work
+    la.lite_attn_fwd(q, k, v, out, tile_m=128, tile_n=64, tau=-3.0, mask_in=m, mask_out=m, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
