@@ -202,7 +202,8 @@ def main():
     ap.add_argument("--tau", type=float, default=-3.0)
     ap.add_argument("--path", choices=("skiplist", "bitmask"), default="skiplist")
     ap.add_argument("--sweep-steps", type=int, default=50, help="steps of the tau sweep (0: skip)")
-    ap.add_argument("--cpu-rows", type=int, default=0, help="oracle rows for the CPU baseline (0: 2 per thread)")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="oracle rows for the CPU baseline (0: 6 per thread, ~10-15 s on the GPU box's 16 threads)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--dense-variants", action="store_true",
                     help="also time every bf16 kernel instantiation (head_dim, key-tile width) dense at 32,768 "
@@ -421,7 +422,7 @@ def main():
         import numpy as np
         from oracle import oracle
         nth = cpu_threads()
-        nrows = args.cpu_rows or 2 * nth
+        nrows = args.cpu_rows or 6 * nth
         q0, k0, v0 = step0
         rng = np.random.default_rng(0)
         rows = np.sort(rng.choice(wl.rows, size=min(nrows, wl.rows), replace=False)).astype(np.int64)
