@@ -9,7 +9,9 @@ buffers, with eager work and a synchronisation between replays, and must give
 exactly what the eager calls give at the same step (every kernel here is
 deterministic: one workgroup per output row, no atomics on outputs).  A
 second graph captures reset + forward: eager calls between its replays grow
-the mask, and the captured reset has to clear it every time.
+the mask, and the captured reset has to clear it every time.  Last, two layers
+stepping on two streams at once must match the same calls made one after the
+other.
 """
 
 import sys
@@ -92,3 +94,34 @@ def test_graph_replays_equal_eager_steps(name, wl, use_skiplist):
             attn(q, k, v)                      # eager steps on the same mask
         torch.cuda.synchronize()
         assert torch.equal(attn.mask, eager[-1][2])
+
+
+def test_two_streams_equal_sequential_calls():
+    """No state in the library, all work on the caller's stream: two layers
+    stepping their own masks on two streams at once give exactly what they
+    give one after the other (streams at the default priority)."""
+    wls = [configs.scaled(configs.C2, (4, 10, 25), heads=3, batch=1, steps=3),
+           configs.scaled(configs.C3, (3, 10, 30), heads=2, batch=1, steps=3)]
+    kws = [dict(threshold=-3.0, tile_m=w.tile_m, tile_n=w.tile_n, use_skiplist=s) for w, s in zip(wls, (True, False))]
+    steps = [_steps(w) for w in wls]
+    # one after the other, on the current stream
+    seq = []
+    for kw, st in zip(kws, steps):
+        a = la.LiteAttention(**kw)
+        seq.append([(a(q, k, v).clone(), a.mask.clone()) for q, k, v in st])
+    torch.cuda.synchronize()
+    # both layers at once, each on its own stream
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    layers = [la.LiteAttention(**kw) for kw in kws]
+    res = [[], []]
+    torch.cuda.synchronize()
+    for t in range(3):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                q, k, v = steps[i][t]
+                res[i].append((layers[i](q, k, v).clone(), layers[i].mask.clone()))
+    torch.cuda.synchronize()
+    for i in range(2):
+        for t in range(3):
+            assert torch.equal(res[i][t][0], seq[i][t][0]), "layer %d step %d output" % (i, t)
+            assert torch.equal(res[i][t][1], seq[i][t][1]), "layer %d step %d mask" % (i, t)
