@@ -147,6 +147,37 @@ def test_build_skiplist_matches_reference(tk):
         assert list(got[r, 1:1 + counts[r]]) == list(lists[r])
 
 
+@pytest.mark.parametrize("name", ["c4_bf16_76k", "c5_bf16_76k_pair"])
+def test_build_skiplist_full_size(name):
+    """The Skip-List build at the benchmark's shapes (23,640 and 47,280 rows of
+    591 tiles): every row by properties that fix the list (the count is the
+    number of live tiles; the entries are strictly descending and all live, so
+    they are exactly the live tiles in visiting order), and 200 sampled rows
+    against the oracle's reference."""
+    wl = configs.ALL[name]
+    desc = la.make_desc(wl.batch, wl.seqlen, wl.heads, wl.head_dim, wl.tile_m, wl.tile_n, la.LITE_BF16)
+    mask = synth.random_mask(wl.rows, wl.tk, 0.6, seed=17)
+    sl = torch.full((la.lite_attn_skiplist_len(desc),), -9, dtype=torch.int32, device="cuda")
+    la.lite_attn_build_skiplist(desc, mask.cuda().reshape(-1), sl)
+    got = sl.cpu().numpy().reshape(wl.rows, 1 + wl.tk)
+    words = mask.numpy().view(np.uint32).reshape(wl.rows, wl.mask_words)
+    bits = np.unpackbits(words.view(np.uint8), bitorder="little").reshape(wl.rows, -1)[:, :wl.tk].astype(bool)
+    live = ~bits
+    counts = got[:, 0]
+    assert np.array_equal(counts, live.sum(axis=1))
+    pos = np.arange(wl.tk)[None, :]
+    valid = pos < counts[:, None]
+    ent = np.where(valid, got[:, 1:], -1)
+    assert np.all(ent[valid] >= 0) and np.all(ent[valid] < wl.tk)
+    assert np.all(np.where(valid[:, 1:], ent[:, 1:] < ent[:, :-1], True))          # strictly descending
+    rows_idx = np.broadcast_to(np.arange(wl.rows)[:, None], ent.shape)
+    assert np.all(live[rows_idx[valid], ent[valid]])                                # every entry live
+    sample = np.random.default_rng(3).choice(wl.rows, 200, replace=False)
+    rc, rl = oracle.skiplist(words[sample], wl.tk)
+    for i, r in enumerate(sample):
+        assert got[r, 0] == rc[i] and list(got[r, 1:1 + rc[i]]) == list(rl[i])
+
+
 def test_reset_mask_clears_every_word():
     desc = la.make_desc(2, 5000, 3, 128, 128, 128, la.LITE_BF16)
     m = torch.full((la.lite_attn_mask_words(desc) + 8,), -1, dtype=torch.int32, device="cuda")
