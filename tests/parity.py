@@ -131,6 +131,27 @@ def check_full(q, k, v, BM, BN, tau, scale, mask_in=None, use_skiplist=False, nt
     return stats, orc
 
 
+def check_all_rows(gpu, v, mask_in, Tk):
+    """Properties every row must have at any size, for the rows the oracle
+    does not recompute: each output is a convex combination of V rows (so
+    within V's per-(batch, head, dim) range, up to bf16 rounding), every lse is
+    finite (no row of these masks is fully skipped), and mask_out keeps every
+    bit of mask_in and no bit past the last tile."""
+    out, lse, mo = gpu
+    vf = v.float()
+    vmin, vmax = vf.amin(dim=1, keepdim=True), vf.amax(dim=1, keepdim=True)      # [B, 1, H, D]
+    slack = 1e-2 * torch.maximum(vmin.abs(), vmax.abs()) + 1e-3
+    of = out.float()
+    assert bool(torch.isfinite(of).all()), "non-finite output"
+    assert bool(((of >= vmin - slack) & (of <= vmax + slack)).all()), "an output outside the range of V"
+    assert bool(torch.isfinite(lse).all()), "non-finite lse"
+    if mo is not None:
+        mi = np.zeros_like(mo) if mask_in is None else np.asarray(mask_in).view(np.uint32).reshape(mo.shape)
+        assert not np.any(mi & ~mo), "mask_out dropped a bit of mask_in"
+        if Tk % 32:
+            assert not np.any(mo[:, -1] >> np.uint32(Tk % 32)), "bits past the last tile"
+
+
 def sample_rows(B, H, Tq, n, seed):
     rng = np.random.default_rng(seed)
     rows = set()

@@ -232,7 +232,8 @@ def test_fp32_long_sequences_sampled_rows(N, density, skiplist):
 @pytest.mark.parametrize("name", ["c3_bf16_33k", "c4_bf16_76k", "c5_bf16_76k_pair"])
 def test_full_size_sampled_rows(name):
     """Full-size workloads in the benchmark's launch configuration: step 0 (empty
-    mask) and a step from a synthetic 60%-sparse mask, on sampled rows."""
+    mask) and a step from a synthetic 60%-sparse mask, on sampled rows against
+    the oracle, and every row by properties."""
     wl = configs.ALL[name]
     tr = synth.Trajectory(wl, "cuda")
     q, k, v = tr.tensors()
@@ -250,6 +251,8 @@ def test_full_size_sampled_rows(name):
         st = pa.compare_rows(gpu, orc, rows, wl.batch, wl.seqlen, wl.heads, wl.tile_m, wl.tile_n, tau,
                              torch.bfloat16)
         log("  ", st)
+        pa.check_all_rows(gpu, vc, mask, wl.tk)
+        log("   every row: outputs within V's range, lse finite, marks kept")
 
 
 def test_binding_refuses_short_or_mistyped_buffers():
