@@ -8,7 +8,8 @@ compared with the oracle at the usual bars: outputs within 2e-2 (bf16) /
 1e-5 (fp32) max-abs, lse within 1e-3 / 1e-5, masks bit-exact except tiles
 whose oracle margin is within 1e-3 of tau.  Inputs are plain Gaussian
 q, k (std 1.5) and v (std 1); the configurations come from a fixed seed, so
-the sweep is the same on every run.
+the sweep is the same on every run.  A second sweep passes q, k, v and out as
+sequence slices of larger batch-2 tensors, through the batch strides.
 """
 
 import math
@@ -18,6 +19,8 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import oracle
+from temporal_block_sparse_amd import lite_attn as la
 from temporal_block_sparse_amd import synth
 from tests import parity as pa
 
@@ -86,3 +89,62 @@ def test_random_configuration(case):
     stats, _ = pa.check_full(q, k, v, c["BM"], c["BN"], c["tau"], 1.0 / math.sqrt(c["D"]), mask_in=mask,
                              use_skiplist=c["skiplist"], must_do=c["must_do"], must_skip=c["must_skip"])
     print("   ", stats, flush=True)
+
+
+def _strided_cases():
+    rng = np.random.default_rng(20261204)
+    out = []
+    for i in range(8):
+        D = int(rng.choice([64, 128]))
+        BN = int(rng.choice([64, 128]))
+        Nq, Nk = int(rng.integers(1, 500)), int(rng.integers(1, 600))
+        out.append(dict(name="strided-%d" % i, D=D, BN=BN, H=int(rng.choice([1, 2, 3])), Nq=Nq, Nk=Nk,
+                        q_off=int(rng.integers(0, 200)), k_off=int(rng.integers(0, 200)),
+                        extra=int(rng.integers(1, 150)), density=float(rng.choice([0.0, 0.3, 0.7])),
+                        tau=float(rng.choice([-math.inf, -3.0, -1.0])), skiplist=bool(rng.integers(0, 2)),
+                        seed=200 + i))
+    return out
+
+
+STRIDED = _strided_cases()
+
+
+@pytest.mark.parametrize("case", STRIDED, ids=[c["name"] for c in STRIDED])
+def test_random_strided_slices(case):
+    """q, k, v and out as sequence slices of larger batch-2 tensors (batch
+    strides larger than an entry): the kernel must read and write through the
+    strides, and write nothing outside its output slice."""
+    c = case
+    B, H, D, BM, BN = 2, c["H"], c["D"], 128, c["BN"]
+    Lq, Lk = c["q_off"] + c["Nq"] + c["extra"], c["k_off"] + c["Nk"] + c["extra"]
+    print("  %s: D %d BN %d H %d Nq %d (at %d of %d) Nk %d (at %d of %d) density %.1f tau %g skiplist %s"
+          % (c["name"], D, BN, H, c["Nq"], c["q_off"], Lq, c["Nk"], c["k_off"], Lk, c["density"], c["tau"],
+             c["skiplist"]), flush=True)
+    qf, _, _ = synth.random_qkv(B, Lq, H, D, dtype=torch.bfloat16, seed=c["seed"], scale=1.5, device="cuda")
+    _, kf, vf = synth.random_qkv(B, Lk, H, D, dtype=torch.bfloat16, seed=c["seed"] + 7, scale=1.5, device="cuda")
+    q = qf[:, c["q_off"]:c["q_off"] + c["Nq"]]
+    k, v = kf[:, c["k_off"]:c["k_off"] + c["Nk"]], vf[:, c["k_off"]:c["k_off"] + c["Nk"]]
+    outf = torch.full((B, Lq, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = outf[:, c["q_off"]:c["q_off"] + c["Nq"]]
+    Tq, Tk = -(-c["Nq"] // BM), -(-c["Nk"] // BN)
+    rows, W = B * H * Tq, -(-Tk // 32)
+    mask = synth.random_mask(rows, Tk, c["density"], seed=c["seed"]).numpy().view(np.uint32).reshape(rows, -1)
+    mi = torch.as_tensor(mask.view(np.int32).reshape(-1)).cuda()
+    mo = torch.full_like(mi, 0x5A5A5A5A)
+    lse = torch.full((B, H, c["Nq"]), float("nan"), device="cuda")
+    desc = la.desc_of(q, BM, BN, k, out)
+    sl = None
+    if c["skiplist"]:
+        sl = torch.full((la.lite_attn_skiplist_len(desc),), -7, dtype=torch.int32, device="cuda")
+        la.lite_attn_build_skiplist(desc, mi, sl)
+    scale = 1.0 / math.sqrt(D)
+    la.lite_attn_fwd(q, k, v, out, tile_m=BM, tile_n=BN, tau=c["tau"], softmax_scale=scale, mask_in=mi,
+                     mask_out=mo, skiplist=sl, lse=lse)
+    torch.cuda.synchronize()
+    outside = torch.cat([outf[:, :c["q_off"]].reshape(-1), outf[:, c["q_off"] + c["Nq"]:].reshape(-1)])
+    assert bool(torch.isnan(outside.float()).all()), "the kernel wrote outside its output slice"
+    qc, kc, vc = q.cpu().contiguous(), k.cpu().contiguous(), v.cpu().contiguous()
+    orc = oracle.fwd(qc, kc, vc, BM, BN, c["tau"], scale, mask_in=mask)
+    gpu = (out.cpu().contiguous(), lse.cpu(), mo.cpu().numpy().view(np.uint32).reshape(rows, W))
+    print("   ", pa.compare_rows(gpu, orc, orc["rows"], B, c["Nq"], H, BM, BN, c["tau"], torch.bfloat16,
+                                 Nk=c["Nk"]), flush=True)
