@@ -212,6 +212,8 @@ def main():
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
 
+    if args.steps < 1 or args.warmup < 0 or args.sweep_steps < 0:
+        ap.error("--steps must be at least 1; --warmup and --sweep-steps at least 0")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(the forward shards by heads; see the design notes).", file=sys.stderr)

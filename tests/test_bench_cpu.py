@@ -83,3 +83,9 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert p.returncode == 2
     assert "one GPU" in p.stderr
+
+
+def test_step_count_must_be_positive():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "0"], capture_output=True,
+                       text=True, timeout=120)
+    assert p.returncode == 2 and "--steps must be at least 1" in p.stderr
