@@ -1,4 +1,4 @@
-"""Seeded randomized sweep of the forward against the CPU oracle.
+"""Seeded randomized sweep of the forward against the CPU oracle (80 configurations).
 
 Each case draws a configuration the other tests fix by hand: batch, heads,
 head_dim and key-tile width, query and key lengths (independent, with ragged
@@ -39,26 +39,26 @@ def _ranges(rng, nk):
 def _cases():
     rng = np.random.default_rng(20261203)
     out = []
-    for i in range(24):
+    for i in range(64):
         D = int(rng.choice([64, 128]))
         BN = int(rng.choice([64, 128]))
         out.append(dict(name="bf16-%d" % i, dtype=torch.bfloat16, BM=128, BN=BN, D=D,
                         B=int(rng.choice([1, 2])), H=int(rng.choice([1, 2, 3])),
-                        Nq=int(rng.integers(1, 700)), Nk=int(rng.integers(1, 900)),
+                        Nq=int(rng.integers(1, 1200)), Nk=int(rng.integers(1, 1500)),
                         density=float(rng.choice([0.0, 0.2, 0.5, 0.9])),
                         tau=float(rng.choice([-math.inf, -6.0, -3.0, -1.0, 0.0])),
                         skiplist=bool(rng.integers(0, 2)), seed=i,
-                        must_do=_ranges(rng, 900) if rng.random() < 0.3 else None,
-                        must_skip=_ranges(rng, 900) if rng.random() < 0.3 else None))
-    for i in range(4):
+                        must_do=_ranges(rng, 1500) if rng.random() < 0.3 else None,
+                        must_skip=_ranges(rng, 1500) if rng.random() < 0.3 else None))
+    for i in range(16):
         out.append(dict(name="fp32-%d" % i, dtype=torch.float32, BM=64, BN=64, D=64,
                         B=int(rng.choice([1, 2])), H=int(rng.choice([1, 2])),
-                        Nq=int(rng.integers(1, 400)), Nk=int(rng.integers(1, 400)),
+                        Nq=int(rng.integers(1, 800)), Nk=int(rng.integers(1, 800)),
                         density=float(rng.choice([0.0, 0.3, 0.7])),
                         tau=float(rng.choice([-math.inf, -5.0, -3.0, 0.0])),
                         skiplist=bool(rng.integers(0, 2)), seed=100 + i,
-                        must_do=_ranges(rng, 400) if rng.random() < 0.3 else None,
-                        must_skip=_ranges(rng, 400) if rng.random() < 0.3 else None))
+                        must_do=_ranges(rng, 800) if rng.random() < 0.3 else None,
+                        must_skip=_ranges(rng, 800) if rng.random() < 0.3 else None))
     return out
 
 
