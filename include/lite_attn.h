@@ -164,6 +164,9 @@ size_t lite_attn_skiplist_len(const lite_attn_desc *desc);
  *             tile.
  *   ranges    host, or NULL for none: must-do / must-skip key ranges.
  *   stream    hipStream_t.
+ * With the environment variable LITE_ATTENTION_VERBOSE set to anything other
+ * than "FALSE" ([README] debug flags), each call that passes validation prints
+ * one line describing its launch to stderr.
  */
 int lite_attn_fwd(const lite_attn_desc *desc, const void *q, const void *k, const void *v,
                   const uint32_t *mask_in, uint32_t *mask_out, const int32_t *skiplist,

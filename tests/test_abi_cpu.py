@@ -272,3 +272,19 @@ def test_binding_refuses_short_mask_and_skiplist_buffers():
     # right sizes, host memory: refused for the device
     with pytest.raises(ValueError, match="device tensor expected"):
         la.lite_attn_reset_mask(d, torch.zeros(nw, dtype=torch.int32))
+
+
+def test_verbose_flag_prints_one_line_per_call():
+    """[README] debug flags: LITE_ATTENTION_VERBOSE (not "FALSE") prints the
+    launch of each validated forward on stderr.  Run in a child process, so
+    the C library's stderr can be read; without a GPU the launch itself then
+    fails, after the line."""
+    import subprocess
+    import sys
+    child = ("import ctypes, sys; sys.path.insert(0, %r)\n"
+             "from tests import test_abi_cpu as t\n"
+             "print('rc', t.fwd(t.desc()))\n") % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for flag, want in (("1", True), ("FALSE", False)):
+        env = dict(os.environ, LITE_ATTENTION_VERBOSE=flag, HIP_VISIBLE_DEVICES="")
+        p = subprocess.run([sys.executable, "-c", child], env=env, capture_output=True, text=True, timeout=120)
+        assert ("[lite_attn] fwd bf16" in p.stderr) == want, (flag, p.stderr[-500:])
