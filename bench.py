@@ -203,7 +203,7 @@ def main():
     ap.add_argument("--path", choices=("skiplist", "bitmask"), default="skiplist")
     ap.add_argument("--sweep-steps", type=int, default=50, help="steps of the tau sweep (0: skip)")
     ap.add_argument("--cpu-rows", type=int, default=0,
-                    help="oracle rows for the CPU baseline (0: 6 per thread, ~10-15 s on the GPU box's 16 threads)")
+                    help="oracle rows for the CPU baseline (0: 6 per thread, ~10-15 s on 16 host threads)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--dense-variants", action="store_true",
                     help="also time every bf16 kernel instantiation (head_dim, key-tile width) dense at 32,768 "
@@ -215,8 +215,8 @@ def main():
     if args.steps < 1 or args.warmup < 0 or args.sweep_steps < 0:
         ap.error("--steps must be at least 1; --warmup and --sweep-steps at least 0")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the forward shards by heads; see the design notes).", file=sys.stderr)
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(the forward would shard by heads, each GPU running this kernel on its own heads).", file=sys.stderr)
         sys.exit(2)
 
     import torch
