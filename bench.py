@@ -199,7 +199,8 @@ def main():
     ap.add_argument("--workload", default="c4_bf16_76k")
     ap.add_argument("--grid", default=None, help="F,H,W token grid overriding the workload's (same recipe)")
     ap.add_argument("--heads", type=int, default=None, help="head count overriding the workload's")
-    ap.add_argument("--tau", type=float, default=-3.0)
+    ap.add_argument("--tau", type=float, default=None,
+                    help="threshold of every step (default: the workload's per-step schedule if it has one, else -3)")
     ap.add_argument("--path", choices=("skiplist", "bitmask"), default="skiplist")
     ap.add_argument("--sweep-steps", type=int, default=50, help="steps of the tau sweep (0: skip)")
     ap.add_argument("--cpu-rows", type=int, default=0,
@@ -238,12 +239,20 @@ def main():
         wl = configs.scaled(wl, grid, heads=args.heads, name="%s_grid%s_h%d" % (
             wl.name, "x".join(str(x) for x in grid), args.heads or wl.heads))
     bf16 = wl.dtype == "bf16"   # else the fp32 path (fp64 arithmetic on the fp64 matrix cores)
+
+    def tau_at(t):
+        """Threshold of trajectory step t: --tau, else the workload's schedule, else -3."""
+        if args.tau is not None:
+            return args.tau
+        return wl.tau_at(t) if wl.tau_schedule is not None else -3.0
+    tau_desc = (args.tau if args.tau is not None else
+                ("schedule %g..%g" % wl.tau_schedule if wl.tau_schedule is not None else -3.0))
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP64_TFLOPS
     dev = torch.device("cuda")
     scale = 1.0 / math.sqrt(wl.head_dim)
     K, W = args.steps, args.warmup
-    log("[bench] workload %s: B=%d H=%d N=%d d=%d tile %dx%d, tau %g, path %s, warmup %d, steps %d"
-        % (wl.name, wl.batch, wl.heads, wl.seqlen, wl.head_dim, wl.tile_m, wl.tile_n, args.tau, args.path, W, K))
+    log("[bench] workload %s: B=%d H=%d N=%d d=%d tile %dx%d, tau %s, path %s, warmup %d, steps %d"
+        % (wl.name, wl.batch, wl.heads, wl.seqlen, wl.head_dim, wl.tile_m, wl.tile_n, tau_desc, args.path, W, K))
 
     tr = synth.Trajectory(wl, dev)
     desc = la.make_desc(wl.batch, wl.seqlen, wl.heads, wl.head_dim, wl.tile_m, wl.tile_n,
@@ -271,7 +280,7 @@ def main():
         q, k, v = tr.tensors()
         if t == 0:
             step0 = (q, k, v)
-        step(q, k, v, warm_mask[t % 2], warm_mask[(t + 1) % 2], args.tau)
+        step(q, k, v, warm_mask[t % 2], warm_mask[(t + 1) % 2], tau_at(t))
         tr.advance()
     if W == 0:
         step0 = tr.tensors()
@@ -291,7 +300,7 @@ def main():
     t0 = time.perf_counter()
     for t in range(K):
         q, k, v = inputs[t]
-        step(q, k, v, masks[t], masks[t + 1], args.tau, evs[t])
+        step(q, k, v, masks[t], masks[t + 1], tau_at(W + t), evs[t])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = [a.elapsed_time(b) for a, b in evs]
@@ -358,7 +367,14 @@ def main():
     # ---- tau sweep over a trajectory (kernel time per step, per threshold) ----
     sweep = None
     if args.sweep_steps > 0:
-        taus = list(wl.taus) if wl.taus else [args.tau]
+        # thresholds of the sweep: the workload's list, or dense and its schedule
+        # (None stands for the schedule), or the one threshold given
+        if wl.taus:
+            taus = list(wl.taus)
+        elif wl.tau_schedule is not None and args.tau is None:
+            taus = [-math.inf, None]
+        else:
+            taus = [-math.inf, tau_at(0)]
         tr2 = synth.Trajectory(wl, dev)
         sm = {tau: [torch.zeros(nw, dtype=torch.int32, device=dev) for _ in range(2)] for tau in taus}
         rec = {tau: [] for tau in taus}
@@ -368,13 +384,13 @@ def main():
             for tau in taus:
                 m_in, m_out = sm[tau][t % 2], sm[tau][(t + 1) % 2]
                 ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                if math.isinf(tau):
+                if tau is not None and math.isinf(tau):
                     ev[0].record()
                     la.lite_attn_fwd(q, k, v, out, tile_m=wl.tile_m, tile_n=wl.tile_n, tau=tau, softmax_scale=scale)
                     ev[1].record()
                     pend.append((tau, ev, None))
                 else:
-                    step(q, k, v, m_in, m_out, tau, ev)
+                    step(q, k, v, m_in, m_out, wl.tau_at(t) if tau is None else tau, ev)
                     pend.append((tau, ev, m_in))
             torch.cuda.synchronize()
             for tau, ev, m_in in pend:
@@ -392,7 +408,8 @@ def main():
         for tau in taus:
             tms = [x[0] for x in rec[tau]]
             fl = [x[1] for x in rec[tau]]
-            ent = {"tau": None if math.isinf(tau) else tau, "steps": len(tms), "kernel_ms_total": round(sum(tms), 3),
+            label = tau_desc if tau is None else (None if math.isinf(tau) else tau)   # None: -inf (dense)
+            ent = {"tau": label, "steps": len(tms), "kernel_ms_total": round(sum(tms), 3),
                    "sparsity_first": round(1 - fl[0] / dense_flops, 4), "sparsity_last": round(1 - fl[-1] / dense_flops, 4),
                    "sparsity_mean": round(1 - sum(fl) / (dense_flops * len(fl)), 4),
                    "tflops_live": round(sum(fl) / (sum(tms) * 1e-3) / 1e12, 1),
@@ -430,7 +447,7 @@ def main():
         rows = np.sort(rng.choice(wl.rows, size=min(nrows, wl.rows), replace=False)).astype(np.int64)
         qc, kc, vc = q0.cpu(), k0.cpu(), v0.cpu()
         t0c = time.perf_counter()
-        res = oracle.fwd(qc, kc, vc, wl.tile_m, wl.tile_n, args.tau, scale, rows=rows, nthreads=nth)
+        res = oracle.fwd(qc, kc, vc, wl.tile_m, wl.tile_n, tau_at(0), scale, rows=rows, nthreads=nth)
         tc = time.perf_counter() - t0c
         tq = wl.tq
         rf = 0.0
@@ -451,7 +468,7 @@ def main():
         "dtype": "bf16" if bf16 else "fp64", "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "seq_len": wl.seqlen,
                    "grid": list(wl.grid), "head_dim": wl.head_dim, "tile": "%dx%d" % (wl.tile_m, wl.tile_n),
-                   "tau": args.tau, "path": args.path, "timed_steps": [W, W + K - 1]},
+                   "tau": tau_desc, "path": args.path, "timed_steps": [W, W + K - 1]},
         "pct_mfma_peak": round(100.0 * value / peak, 2),
         "speedup_vs_dense": round(sum(dense_ms) / sum(kern_ms), 3),
         "dense_kernel_ms": round(sum(dense_ms) / K, 3), "kernel_ms": round(sum(kern_ms) / K, 3),

@@ -89,3 +89,15 @@ def test_step_count_must_be_positive():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "0"], capture_output=True,
                        text=True, timeout=120)
     assert p.returncode == 2 and "--steps must be at least 1" in p.stderr
+
+
+def test_every_workload_gets_to_its_first_gpu_call():
+    """The host-side set-up of each workload (arguments, threshold schedule,
+    descriptor, log line) runs cleanly; with no GPU visible the run then stops
+    at its first device allocation."""
+    for name in configs.ALL:
+        env = dict(os.environ, HIP_VISIBLE_DEVICES="")
+        p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", name, "--steps", "1",
+                            "--warmup", "0", "--sweep-steps", "0", "--no-cpu"], env=env, capture_output=True,
+                           text=True, timeout=300)
+        assert "[bench] workload %s:" % name in p.stderr, (name, p.stderr[-1500:])
