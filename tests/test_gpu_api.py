@@ -1,0 +1,87 @@
+"""The per-layer class mirroring the README's Python API, on the GPU, against
+the oracle step by step: the carried Skip-Mask, set_threshold,
+enable_skip_optimization(False) (plain attention, mask untouched) and
+reset_skip_state."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from temporal_block_sparse_amd import configs, synth
+from temporal_block_sparse_amd import lite_attn as la
+from tests import parity as pa
+
+pytestmark = pytest.mark.gpu
+
+
+def test_layer_class_against_the_oracle():
+    wl = configs.scaled(configs.C3, (3, 10, 30), heads=2, batch=1, steps=4)
+    tr = synth.Trajectory(wl, "cpu")
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    attn = la.LiteAttention(threshold=-3.0, tile_m=wl.tile_m, tile_n=wl.tile_n)
+    mask = np.zeros((wl.rows, wl.mask_words), np.uint32)
+    steps = []
+    for t in range(4):
+        if t:
+            tr.advance()
+        steps.append(tr.tensors())
+
+    def step(q, k, v, tau, mask_in):
+        print("   oracle step, tau %g" % tau, flush=True)
+        sys.stdout.flush()
+        return oracle.fwd(q, k, v, wl.tile_m, wl.tile_n, tau, scale, mask_in=mask_in)
+
+    def gpu_mask():
+        return attn.mask.cpu().numpy().view(np.uint32).reshape(wl.rows, -1)
+
+    def near_tau_ok(got, orc, tau):
+        """Marks equal the oracle's, except tiles whose margin is within 1e-3 of tau."""
+        want = orc["mask_out"]
+        diff = got ^ want
+        for r, kt in zip(*np.nonzero(np.unpackbits(diff.view(np.uint8), bitorder="little").reshape(wl.rows, -1))):
+            assert abs(orc["margin"][r, kt] - tau) <= pa.NEAR_TAU, "mask differs at row %d tile %d" % (r, kt)
+
+    # threshold -3 over two steps: the carried mask and the outputs
+    for t in range(2):
+        q, k, v = steps[t]
+        out = attn(q.cuda(), k.cuda(), v.cuda())
+        orc = step(q, k, v, -3.0, mask)
+        o_ref, _ = oracle.unpack_rows(orc, wl.batch, wl.seqlen, wl.heads, wl.tile_m)
+        assert float(np.abs(out.cpu().double().numpy() - o_ref).max()) <= pa.TOL_OUT[torch.bfloat16]
+        near_tau_ok(gpu_mask(), orc, -3.0)
+        mask = gpu_mask().copy()            # follow the GPU's mask (equal off near-tau ties)
+    assert mask.any(), "nothing marked: the test would not see the mask carried"
+
+    # skipping off: plain attention, mask untouched
+    attn.enable_skip_optimization(False)
+    q, k, v = steps[2]
+    out = attn(q.cuda(), k.cuda(), v.cuda())
+    orc = step(q, k, v, -math.inf, None)
+    o_ref, _ = oracle.unpack_rows(orc, wl.batch, wl.seqlen, wl.heads, wl.tile_m)
+    assert float(np.abs(out.cpu().double().numpy() - o_ref).max()) <= pa.TOL_OUT[torch.bfloat16]
+    assert np.array_equal(gpu_mask(), mask)
+    attn.enable_skip_optimization(True)
+
+    # a looser threshold marks more, on the carried mask
+    attn.set_threshold(-1.0)
+    out = attn(q.cuda(), k.cuda(), v.cuda())
+    orc = step(q, k, v, -1.0, mask)
+    o_ref, _ = oracle.unpack_rows(orc, wl.batch, wl.seqlen, wl.heads, wl.tile_m)
+    assert float(np.abs(out.cpu().double().numpy() - o_ref).max()) <= pa.TOL_OUT[torch.bfloat16]
+    near_tau_ok(gpu_mask(), orc, -1.0)
+    assert not np.any(mask & ~gpu_mask())
+
+    # reset: every tile live again, and the next call starts from an empty mask
+    attn.reset_skip_state()
+    torch.cuda.synchronize()
+    assert not gpu_mask().any()
+    q, k, v = steps[3]
+    out = attn(q.cuda(), k.cuda(), v.cuda())
+    orc = step(q, k, v, -1.0, None)
+    o_ref, _ = oracle.unpack_rows(orc, wl.batch, wl.seqlen, wl.heads, wl.tile_m)
+    assert float(np.abs(out.cpu().double().numpy() - o_ref).max()) <= pa.TOL_OUT[torch.bfloat16]
+    near_tau_ok(gpu_mask(), orc, -1.0)
