@@ -7,7 +7,9 @@ reference below is a direct restatement of "list the live key tiles in the
 order the kernel visits them".
 
 Pages: [README] = the LiteAttention project README (moonmath-ai/LiteAttention);
-[ABSTRACT] = arXiv 2511.11062 abstract.
+[ABSTRACT] = arXiv 2511.11062 abstract; [SKILL] = the "Lite Attention
+Temporal Sparse" skill page (its "Step 3: Error Calibration" gives the budget
+multipliers used by error_budgets).
 """
 
 import ctypes
@@ -228,22 +230,27 @@ def merge(outs, lses):
 
 
 def error_budgets(num_steps, early_step_ratio=0.3):
-    """Per-timestep error-budget multipliers ([README] "Error Calibration" /
-    "Accumulated-Error Calibration"): for the first floor(T*r) steps the
-    multiplier rises linearly from 0.5 (at step 0) towards 1.0; every later
-    step gets 1.0.  Earlier steps, which weigh more on the final video, get
-    the tighter budgets."""
-    n_early = int(num_steps * early_step_ratio)
-    out = []
-    for t in range(num_steps):
-        out.append(0.5 + 0.5 * (t / n_early) if t < n_early else 1.0)
-    return out
+    """Per-timestep error-budget multipliers, in the form the "Lite Attention
+    Temporal Sparse" skill page gives in "Implementation Steps", "Step 3: Error
+    Calibration" (the LiteAttention README's "Error Calibration" says only that
+    earlier timesteps get stricter bounds; it prints no schedule).
+
+    With n = floor(T * r) early steps (T = num_steps, r = early_step_ratio):
+        b_t = min(1, 0.5 + 0.5 * t / n)    for n >= 1,
+    i.e. b_0 = 0.5, a rise of 0.5 / n per step, and 1 from t = n on; when
+    T * r < 1 there is no early step and every b_t is 1."""
+    n = math.floor(num_steps * early_step_ratio)
+    if n < 1:
+        return [1.0] * num_steps
+    return [min(1.0, 0.5 + 0.5 * t / n) for t in range(num_steps)]
 
 
 def calibrate(steps, tile_m, tile_n, scale, base_error, taus, early_step_ratio=0.3, nthreads=None):
-    """Per-timestep thresholds from per-step output-error budgets ([README]
-    "Error Calibration" / "Accumulated-Error Calibration": variable error
-    budgets per timestep, stricter early), on given inputs.
+    """Per-timestep thresholds from per-step output-error budgets, on given
+    inputs.  [README] "Error Calibration": the timesteps get variable error
+    budgets, stricter early; the multipliers are the skill page's (see
+    error_budgets), and how a budget picks a threshold is this module's
+    reading (the pages do not say).
 
     steps: list of (q, k, v) per denoising step.  taus: candidate thresholds.
     The budget of step t is base_error * error_budgets(T)[t].  At step t, with

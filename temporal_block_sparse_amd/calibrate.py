@@ -1,15 +1,16 @@
 """Per-timestep threshold calibration from output-error budgets.
 
-LiteAttention README, "Error Calibration" ("Accumulated-Error Calibration" in
-the architecture overview): denoising steps get variable error budgets, with
-tighter budgets on the early steps, which weigh more on the final video.
+LiteAttention README, "Error Calibration": denoising steps get variable error
+budgets, with stricter bounds on the early steps.  The README gives no
+schedule; the multipliers here are the ones the "Lite Attention Temporal
+Sparse" skill page gives in "Implementation Steps", "Step 3: Error
+Calibration" (its "Architecture Overview" calls the idea Accumulated-Error
+Calibration): with n = floor(T * early_step_ratio) early steps, step t gets
+min(1, 0.5 + 0.5 * t / n), and every step gets 1 when n = 0.
 
-The budget multiplier of step t follows the README's printed schedule: over
-the first int(T * early_step_ratio) steps it rises linearly from 0.5 at step
-0, every later step gets 1.0.  The calibration turns the budgets into
-thresholds on given inputs (synthetic here; no model is needed): at step t,
-with the Skip-Mask carried from the earlier steps, a candidate threshold is
-run through the forward, the marks it would add are applied at once, and the
+The calibration turns the budgets into thresholds on given inputs (synthetic
+here; no model is needed): at step t, with the Skip-Mask carried from the
+earlier steps, a candidate threshold is run through the forward, the marks it would add are applied at once, and the
 relative error of that output against plain attention,
     || out(marks) - out(nothing skipped) ||_F / || out(nothing skipped) ||_F,
 is compared with base_error * multiplier(t).  The step takes the largest
@@ -26,9 +27,11 @@ from . import lite_attn as la
 
 
 def error_budgets(num_steps, early_step_ratio=0.3):
-    """Budget multiplier per timestep (README "Error Calibration")."""
-    n_early = int(num_steps * early_step_ratio)
-    return [0.5 + 0.5 * t / n_early if t < n_early else 1.0 for t in range(num_steps)]
+    """Budget multiplier per timestep: min(1, 0.5 + 0.5 * t / n) with
+    n = floor(T * r) early steps, all 1 when n = 0 (skill page "Lite Attention
+    Temporal Sparse", Step 3: Error Calibration)."""
+    n = math.floor(num_steps * early_step_ratio)
+    return [1.0 if n < 1 else min(1.0, 0.5 + 0.5 * t / n) for t in range(num_steps)]
 
 
 def _rel_error(a, b):

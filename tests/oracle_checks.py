@@ -438,8 +438,10 @@ def check_merge():
 
 
 def check_error_budgets():
-    """[README] Error Calibration: over the first int(T*ratio) steps the
-    multiplier goes 0.5 + 0.5*t/int(T*ratio); later steps get 1.0."""
+    """Budget multipliers of the skill page "Lite Attention Temporal Sparse"
+    (Implementation Steps, Step 3: Error Calibration), value by value: over
+    the first floor(T*ratio) steps the multiplier goes 0.5 + 0.5*t/floor(T*ratio),
+    later steps get 1.0, and with no early step every step gets 1.0."""
     fails = []
     b = oracle.error_budgets(50, 0.3)
     if not (len(b) == 50 and b[0] == 0.5 and b[1] == 0.5 + 0.5 / 15 and b[14] == 0.5 + 0.5 * 14 / 15

@@ -90,9 +90,9 @@ PY_MUTANTS = [
     ("merge lse is the max", "lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, s)))",
      "lse = np.where(empty, -np.inf, m_safe)"),
     ("merge weights by lse, not exp", "w = np.exp(L - m_safe)", "w = np.where(np.isneginf(L), 0.0, np.exp(L - m_safe) * 0 + 1)"),
-    ("budgets reach 1.0 inside the early steps", "0.5 + 0.5 * (t / n_early)", "0.5 + 0.5 * (t / max(n_early - 1, 1))"),
-    ("budgets rounded early count", "n_early = int(num_steps * early_step_ratio)", "n_early = round(num_steps * early_step_ratio)"),
-    ("budgets loosest first", "0.5 + 0.5 * (t / n_early)", "1.0 - 0.5 * (t / n_early)"),
+    ("budgets reach 1.0 inside the early steps", "min(1.0, 0.5 + 0.5 * t / n)", "min(1.0, 0.5 + 0.5 * t / max(n - 1, 1))"),
+    ("budgets rounded early count", "n = math.floor(num_steps * early_step_ratio)", "n = round(num_steps * early_step_ratio)"),
+    ("budgets loosest first", "min(1.0, 0.5 + 0.5 * t / n)", "min(1.0, 1.0 - 0.5 * t / n)"),
     ("calibration takes the smallest feasible tau", "cands = sorted(set(float(t) for t in taus), reverse=True)",
      "cands = sorted(set(float(t) for t in taus))"),
     ("calibration forgets the carried mask", "        mask = m2\n    return out", "        mask = None\n    return out"),

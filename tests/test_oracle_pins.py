@@ -193,7 +193,7 @@ def test_lse_merge_of_key_splits_is_full_attention():
     assert oc.check_merge() == []
 
 
-def test_error_budgets_follow_the_printed_schedule():
+def test_error_budgets_follow_the_skill_page_schedule():
     assert oc.check_error_budgets() == []
 
 
