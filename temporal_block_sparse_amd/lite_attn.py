@@ -149,10 +149,17 @@ def _bshd(t):
     along the sequence such as q[:, :text_len]."""
     if t.dim() != 4:
         raise ValueError("BSHD tensor expected")
-    _on_device(t)
     B, N, H, D = t.shape
     if N > 1 and t.stride(1) != H * D or H > 1 and t.stride(2) != D or D > 1 and t.stride(3) != 1:
         raise ValueError("each batch entry must be a contiguous [N][H][D] block")
+    # The C ABI reads a batch stride of 0 as "dense", so a batch-expanded
+    # tensor (stride 0, e.g. k.expand(2, ...)) would make the kernels read or
+    # write a whole batch entry past the allocation: refuse any stride that
+    # lets batch entries overlap.
+    if B > 1 and N * H * D > 0 and t.stride(0) < N * H * D:
+        raise ValueError("batch entries overlap (batch stride %d < %d elements); pass a tensor whose batch "
+                         "entries are separate, e.g. .contiguous()" % (t.stride(0), N * H * D))
+    _on_device(t)
     return B, N, H, D, (t.stride(0) if B > 1 else 0), ctypes.c_void_p(t.data_ptr())
 
 
@@ -284,12 +291,16 @@ class LiteAttention:
     layer, never shared -- updated in place by each call.  `threshold` is in
     natural-log units (README ablation: -10, -3, 0); thresholds above 0 need
     LITE_ATTENTION_DEBUG.  With skipping disabled the call is plain attention
-    and the mask is neither read nor written.  `use_skiplist` walks the
+    and the mask is neither read nor written.  `max_batch_size` (README
+    constructor argument) bounds the batch a call may pass: the skip state
+    holds one mask row per (batch entry, head, q-tile).  `use_skiplist` walks the
     compacted Skip-List (rebuilt from the mask before each call) instead of
     the bitmask.  must_do_list / must_skip_list are the README's key ranges."""
 
-    def __init__(self, enable_skipping=True, threshold=-10.0, tile_m=128, tile_n=128, use_skiplist=False):
+    def __init__(self, enable_skipping=True, threshold=-10.0, max_batch_size=4, tile_m=128, tile_n=128,
+                 use_skiplist=False):
         self.enable_skipping = enable_skipping
+        self.max_batch_size = int(max_batch_size)
         self.threshold = float(threshold)
         self.tile_m, self.tile_n = tile_m, tile_n
         self.use_skiplist = use_skiplist
@@ -308,6 +319,33 @@ class LiteAttention:
         if self.mask is not None:
             lite_attn_reset_mask(self._desc, self.mask)
 
+    def skip_state(self):
+        """The layer's skip state for a checkpoint: a host copy of the Skip-Mask
+        and the shape key it belongs to (batch, seqlen, heads, head_dim, tile_m,
+        tile_n, dtype, seqlen_kv), or None before the first skipping call.
+        Plain tensors and ints: torch.save / torch.load(weights_only=True)
+        round-trip it."""
+        if self.mask is None:
+            return None
+        return {"key": tuple(int(x) for x in self._key), "mask": self.mask.cpu()}
+
+    def load_skip_state(self, state, device=None):
+        """Restore a state from skip_state() (None clears it).  A later call
+        with other shapes starts again from an empty mask, as it would after
+        any change of shape."""
+        if state is None:
+            self._key = self._desc = self.mask = self.skiplist = None
+            return
+        key = tuple(int(x) for x in state["key"])
+        d = make_desc(*key[:7], seqlen_kv=key[7])
+        mask = state["mask"]
+        if mask.dtype != torch.int32 or mask.numel() != lite_attn_mask_words(d):
+            raise ValueError("skip state does not match its shape key")
+        device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self._key, self._desc = key, d
+        self.mask = mask.to(device).contiguous()
+        self.skiplist = alloc_skiplist(d, device) if self.use_skiplist else None
+
     def _state_for(self, q, k):
         d = desc_of(q, self.tile_m, self.tile_n, k)
         key = (d.batch, d.seqlen, d.heads, d.head_dim, d.tile_m, d.tile_n, d.dtype, d.seqlen_kv)
@@ -321,6 +359,8 @@ class LiteAttention:
 
     def __call__(self, q, k, v, scale=None, return_softmax_lse=False, out=None, must_do_list=None,
                  must_skip_list=None):
+        if q.shape[0] > self.max_batch_size:
+            raise ValueError("batch %d larger than max_batch_size %d" % (q.shape[0], self.max_batch_size))
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device) if out is None else out
         lse = None
         if return_softmax_lse:
@@ -350,7 +390,8 @@ class SeqParallelLiteAttention:
     def __init__(self, num_nodes, enable_skipping=True, threshold=-10.0, max_batch_size=4, **kw):
         self.num_nodes = int(num_nodes)
         self.max_batch_size = int(max_batch_size)
-        self._splits = [LiteAttention(enable_skipping, threshold, **kw) for _ in range(self.num_nodes)]
+        self._splits = [LiteAttention(enable_skipping, threshold, max_batch_size, **kw)
+                        for _ in range(self.num_nodes)]
 
     def set_threshold(self, threshold):
         for s in self._splits:

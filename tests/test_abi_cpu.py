@@ -288,3 +288,43 @@ def test_verbose_flag_prints_one_line_per_call():
         env = dict(os.environ, LITE_ATTENTION_VERBOSE=flag, HIP_VISIBLE_DEVICES="")
         p = subprocess.run([sys.executable, "-c", child], env=env, capture_output=True, text=True, timeout=120)
         assert ("[lite_attn] fwd bf16" in p.stderr) == want, (flag, p.stderr[-500:])
+
+
+@pytest.mark.parametrize("make", [
+    lambda: torch.zeros(1, 300, 2, 64, dtype=torch.bfloat16).expand(2, 300, 2, 64),        # batch stride 0
+    lambda: torch.zeros(1, 600, 2, 64, dtype=torch.bfloat16).as_strided((2, 300, 2, 64), (100 * 128, 128, 64, 1)),
+])
+def test_binding_refuses_overlapping_batch_entries(make):
+    """The C ABI reads a batch stride of 0 as "dense": a batch-expanded tensor
+    would be read (or written) a whole batch entry past its allocation.  The
+    binding refuses any tensor whose batch entries overlap, before it looks at
+    the device or calls the library."""
+    t = make()
+    with pytest.raises(ValueError, match="batch entries overlap"):
+        la._bshd(t)
+    with pytest.raises(ValueError, match="batch entries overlap"):
+        la.desc_of(t, 128, 64)
+    with pytest.raises(ValueError, match="batch entries overlap"):
+        la.lite_attn_fwd(t, t, t, t, tile_m=128, tile_n=64, tau=-3.0)
+    # a sequence slice of a larger tensor keeps a batch stride >= its own entry: not refused by this check
+    sl = torch.zeros(2, 600, 2, 64, dtype=torch.bfloat16)[:, :300]
+    with pytest.raises(ValueError, match="device tensor expected"):
+        la._bshd(sl)
+
+
+def test_layer_classes_refuse_batches_over_max_batch_size():
+    """README Python API: the constructor takes max_batch_size (default 4);
+    a larger batch is refused before anything is allocated or launched."""
+    q = torch.zeros(5, 8, 1, 64, dtype=torch.bfloat16)
+    attn = la.LiteAttention(threshold=-3.0)
+    assert attn.max_batch_size == 4
+    with pytest.raises(ValueError, match="max_batch_size"):
+        attn(q, q, q)
+    assert attn.mask is None
+    attn = la.LiteAttention(True, -3.0, 2)
+    with pytest.raises(ValueError, match="max_batch_size"):
+        attn(q[:3], q[:3], q[:3])
+    sp = la.SeqParallelLiteAttention(num_nodes=2, max_batch_size=2)
+    with pytest.raises(ValueError, match="max_batch_size"):
+        sp(q[:3], q[:3], q[:3], split_idx=0)
+    assert all(s.max_batch_size == 2 for s in sp._splits)
