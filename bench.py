@@ -15,7 +15,14 @@ Printed (one JSON line on stdout):
                    / HIP-event launch duration, against the bf16 MFMA peak;
                    traffic from the committed rocprofv3 counter summary when
                    it was taken on the current kernel source, else null
-  cpu_baseline     the CPU oracle timed on a bounded sample of the same step
+  cpu_baseline     the CPU oracle timed on a bounded sample of the same
+                   trajectory: a fixed set of rows (one per host thread, at
+                   most 16) that the oracle carries from an empty mask through
+                   the warmup and timed steps by itself
+  verification     the timed steps W, W + K/2 and W + K - 1 and a step of each
+                   other threshold of the sweep against those oracle rows:
+                   max-abs output and lse differences, mask mismatches and
+                   near-threshold ties (the same bars as the parity tests)
   tau_sweep        per-threshold trajectories (-inf, -10, -3, 0): sparsity,
                    kernel time, speedup and a least-squares fit of t/t_dense
                    against the live fraction
@@ -96,6 +103,91 @@ def pair_occupancy(mask_words, wl):
     a, b = live[:, 0::2], live[:, 1::2]
     union = torch.maximum(a, b).sum()
     return float((a.sum() + b.sum()) / (2.0 * union)) if union > 0 else 1.0
+
+
+def rows_live_flops(row_masks, rows, wl):
+    """4*d*sum over the sampled rows' live tiles of valid rows x valid cols;
+    row_masks: the rows' mask_in words [nrows, W] (host) or None (all live)."""
+    import numpy as np
+    N, BM, BN, d, Tq, Tk = wl.seqlen, wl.tile_m, wl.tile_n, wl.head_dim, wl.tq, wl.tk
+    vc = np.full(Tk, BN, np.float64)
+    vc[-1] = N - (Tk - 1) * BN
+    f = 0.0
+    for i, r in enumerate(rows):
+        qt = int(r % Tq)
+        vr = min(BM, N - qt * BM)
+        live = vc.sum()
+        if row_masks is not None:
+            bits = np.unpackbits(np.asarray(row_masks[i]).view(np.uint32).view(np.uint8),
+                                 bitorder="little")[:Tk].astype(bool)
+            live = vc[~bits].sum()
+        f += 4.0 * d * vr * live
+    return f
+
+
+class OracleCheck:
+    """The oracle's own trajectory on a fixed sample of rows, and the check of
+    GPU steps against it (the CPU-baseline leg: the oracle's calls are also what
+    cpu_baseline times).  Every row (batch, head, q-tile) is independent, so the
+    oracle carries the sampled rows' masks by itself from an empty mask, from
+    the seeded inputs alone; nothing the GPU computes reaches it.  A GPU step is
+    compared on the rows whose carried mask equals the oracle's at that step
+    (they differ only after a tile within 1e-3 of the threshold, where either
+    decision is correct; such rows are counted as diverged)."""
+
+    def __init__(self, wl, scale, rows, nthreads):
+        from tests import parity as pa
+        self.pa, self.wl, self.scale, self.rows, self.nth = pa, wl, scale, rows, nthreads
+        self.carried = {}          # trajectory label -> mask_in words of the rows at the next step
+        self.results = {}          # (label, step) -> (oracle result, its mask_in words)
+        self.seconds = 0.0
+        self.flops = 0.0
+        self.threads = 0
+
+    def step(self, label, t, q, k, v, tau, keep=False, timed=True):
+        wl = self.wl
+        rm = self.carried.get(label)
+        res = self.pa.oracle_sampled(q, k, v, wl.tile_m, wl.tile_n, tau, self.scale, rm, self.rows,
+                                     nthreads=self.nth)
+        if timed:
+            self.seconds += res["seconds"]
+            self.flops += rows_live_flops(rm, self.rows, wl)
+            self.threads = res["nthreads"]
+        if keep:
+            self.results[(label, t)] = (res, rm)
+        self.carried[label] = res["mask_out"].copy()
+
+    def compare(self, label, t, tau, out, lse, m_in, m_out):
+        """Statistics of the GPU's rows at step t of trajectory `label` against
+        the kept oracle result (m_in/m_out: the GPU's mask words, device)."""
+        import numpy as np
+        pa, wl = self.pa, self.wl
+        res, rm = self.results[(label, t)]
+        W = wl.mask_words
+        g = pa.gpu_rows(out, lse, m_out, self.rows, wl.heads, wl.tile_m)
+        if m_in is not None:
+            import torch
+            idx = torch.as_tensor(self.rows, device=m_in.device)
+            gin = m_in.view(-1, W)[idx].cpu().numpy().view(np.uint32)
+        else:
+            gin = np.zeros((len(self.rows), W), np.uint32)
+        oin = rm if rm is not None else np.zeros((len(self.rows), W), np.uint32)
+        same = np.all(gin == oin, axis=1)
+        sel = np.nonzero(same)[0]
+        st = dict(max_out=0.0, max_lse=0.0, near_tau=0, mask_mismatch=0, nonfinite=0, lse_pattern=0, padding=0)
+        if len(sel):
+            gs = {key: (g[key][sel] if g[key] is not None else None) for key in ("out", "lse", "mask_out")}
+            rs = {key: res[key][sel] for key in ("out", "lse", "margin", "mask_out")}
+            rs["rows"] = self.rows[sel]
+            st = pa.packed_errors(gs, rs, wl.seqlen, wl.tile_m, wl.tk, tau)
+        ok = (st["max_out"] <= pa.TOL_OUT[out.dtype] and st["max_lse"] <= pa.TOL_LSE[out.dtype]
+              and st["mask_mismatch"] == 0 and st["nonfinite"] == 0 and st["lse_pattern"] == 0
+              and st["padding"] == 0)
+        return {"trajectory": label, "step": t, "tau": None if math.isinf(tau) else tau,
+                "rows": len(self.rows), "rows_compared": int(len(sel)), "diverged_rows": int(len(self.rows) - len(sel)),
+                "max_abs_out": round(st["max_out"], 6), "max_lse": round(st["max_lse"], 7),
+                "mask_mismatch": st["mask_mismatch"], "near_tau": st["near_tau"],
+                "nonfinite": st["nonfinite"] + st["lse_pattern"] + st["padding"], "within_bars": bool(ok)}
 
 
 def hbm_entry(b, ms):
@@ -204,8 +296,11 @@ def main():
     ap.add_argument("--path", choices=("skiplist", "bitmask"), default="skiplist")
     ap.add_argument("--sweep-steps", type=int, default=50, help="steps of the tau sweep (0: skip)")
     ap.add_argument("--cpu-rows", type=int, default=0,
-                    help="oracle rows for the CPU baseline (0: 6 per thread, ~10-15 s on 16 host threads)")
-    ap.add_argument("--no-cpu", action="store_true")
+                    help="rows the oracle carries through the trajectory for the CPU baseline and the check of "
+                         "the timed steps (0: one per host thread, at most 16)")
+    ap.add_argument("--check-sweep-steps", type=int, default=3,
+                    help="steps of each other threshold's trajectory the oracle carries; the last is checked")
+    ap.add_argument("--no-cpu", action="store_true", help="no CPU baseline and no oracle check")
     ap.add_argument("--dense-variants", action="store_true",
                     help="also time every bf16 kernel instantiation (head_dim, key-tile width) dense at 32,768 "
                          "tokens x 32 heads")
@@ -274,22 +369,38 @@ def main():
         if ev is not None:
             ev[1].record()
 
+    # ---- the oracle's own trajectory on sampled rows (CPU-baseline leg) ----
+    # It runs on the host between the untimed GPU work, from the seeded inputs
+    # alone, and keeps its results for the timed steps checked afterwards.
+    chk = None
+    check_steps = sorted({W, W + K // 2, W + K - 1})
+    if not args.no_cpu:
+        import numpy as np
+        from tests import parity as pa
+        nth = cpu_threads()
+        nrows = args.cpu_rows or nth
+        rows = pa.sample_rows_in_heads(wl.batch, wl.heads, wl.tq, nrows, max(2, nrows // 4), seed=0)
+        chk = OracleCheck(wl, scale, rows, nth)
+        log("[bench] oracle carries %d sampled rows through steps 0..%d (%d host threads)"
+            % (len(rows), W + K - 1, nth))
+
     # ---- warmup: the first W steps of the trajectory (untimed) ----
-    step0 = None
     for t in range(W):
         q, k, v = tr.tensors()
-        if t == 0:
-            step0 = (q, k, v)
         step(q, k, v, warm_mask[t % 2], warm_mask[(t + 1) % 2], tau_at(t))
+        if chk is not None:
+            chk.step("timed", t, q, k, v, tau_at(t), keep=t in check_steps)
         tr.advance()
-    if W == 0:
-        step0 = tr.tensors()
     if W:
         masks[0].copy_(warm_mask[W % 2])
     # ---- inputs of the K timed steps, resident in HBM before timing ----
     inputs = []
     for t in range(K):
         inputs.append(tr.tensors())
+        if chk is not None:
+            chk.step("timed", W + t, *inputs[-1], tau_at(W + t), keep=W + t in check_steps)
+            if t % 5 == 4:
+                log("[bench] oracle at step %d" % (W + t))
         tr.advance()
     torch.cuda.synchronize()
     log("[bench] inputs ready: %.1f GB resident" % (torch.cuda.memory_allocated() / 1e9))
@@ -347,6 +458,35 @@ def main():
     aux_ev[3][1].record()
     torch.cuda.synchronize()
     dense_ms = [a.elapsed_time(b) for a, b in dev_ms]
+
+    # ---- check of timed steps against the oracle's own trajectory ----
+    # The step is run again (untimed) with lse into check buffers, from the
+    # timed step's mask_in; its mask_out must equal the timed step's bit for bit.
+    checks = []
+    ck_out = ck_lse = ck_mask = None
+    if chk is not None:
+        ck_out = torch.empty_like(out)
+        ck_lse = torch.empty(wl.batch, wl.heads, wl.seqlen, dtype=torch.float32, device=dev)
+        ck_mask = torch.empty(nw, dtype=torch.int32, device=dev)
+
+    def check_step(label, t, q, k, v, m_in, tau, m_timed=None):
+        if sl is not None and m_in is not None:
+            la.lite_attn_build_skiplist(desc, m_in, sl)
+        la.lite_attn_fwd(q, k, v, ck_out, tile_m=wl.tile_m, tile_n=wl.tile_n, tau=tau, softmax_scale=scale,
+                         mask_in=m_in, mask_out=ck_mask if m_in is not None else None,
+                         skiplist=sl if m_in is not None else None, lse=ck_lse)
+        torch.cuda.synchronize()
+        c = chk.compare(label, t, tau, ck_out, ck_lse, m_in, ck_mask if m_in is not None else None)
+        if m_timed is not None:
+            c["mask_out_equals_measured_step"] = bool(torch.equal(ck_mask, m_timed))
+            c["within_bars"] = c["within_bars"] and c["mask_out_equals_measured_step"]
+        checks.append(c)
+        log("[bench] check %s step %d: %s" % (label, t, c))
+
+    if chk is not None:
+        for t in check_steps:
+            q, k, v = inputs[t - W]
+            check_step("timed", t, q, k, v, masks[t - W], tau_at(t), masks[t - W + 1])
     sl_ms = aux_ev[0][0].elapsed_time(aux_ev[0][1]) / 10 if sl is not None else None
     reset_ms = aux_ev[1][0].elapsed_time(aux_ev[1][1]) / 10
     aux = aux_kernels(masks[K], wl, sl_ms, reset_ms, aux_ev[2][0].elapsed_time(aux_ev[2][1]) / 10,
@@ -366,6 +506,7 @@ def main():
 
     # ---- tau sweep over a trajectory (kernel time per step, per threshold) ----
     sweep = None
+    sweep_same_as_timed = None
     if args.sweep_steps > 0:
         # thresholds of the sweep: the workload's list, or dense and its schedule
         # (None stands for the schedule), or the one threshold given
@@ -378,6 +519,10 @@ def main():
         tr2 = synth.Trajectory(wl, dev)
         sm = {tau: [torch.zeros(nw, dtype=torch.int32, device=dev) for _ in range(2)] for tau in taus}
         rec = {tau: [] for tau in taus}
+        # the threshold whose trajectory is the timed one: its sweep masks must
+        # equal the timed run's; the others are checked against the oracle
+        head_tau = None if (wl.tau_schedule is not None and args.tau is None) else tau_at(0)
+        S = min(args.check_sweep_steps, args.sweep_steps)
         for t in range(args.sweep_steps):
             q, k, v = tr2.tensors()
             pend = []
@@ -397,6 +542,20 @@ def main():
                 f = dense_flops if m_in is None else live_flops(m_in, wl)
                 occ = 1.0 if m_in is None else pair_occupancy(m_in, wl)
                 rec[tau].append((ev[0].elapsed_time(ev[1]), f, occ))
+            if t == W + K - 1 and head_tau in sm:
+                sweep_same_as_timed = bool(torch.equal(sm[head_tau][(t + 1) % 2], masks[K]))
+            if chk is not None:
+                for tau in taus:
+                    dense = tau is not None and math.isinf(tau)
+                    if tau == head_tau or t >= (1 if dense else S):
+                        continue
+                    tt = wl.tau_at(t) if tau is None else tau
+                    label = "sweep tau %s" % ("-inf" if dense else tt if tau is not None else "schedule")
+                    last = t == (0 if dense else S - 1)
+                    chk.step(label, t, q, k, v, tt, keep=last, timed=False)
+                    if last:
+                        check_step(label, t, q, k, v, None if dense else sm[tau][t % 2], tt,
+                                   None if dense else sm[tau][(t + 1) % 2])
             if t % 10 == 0:
                 log("[bench] sweep step %d/%d" % (t, args.sweep_steps))
             tr2.advance()
@@ -435,30 +594,29 @@ def main():
                                                       "points": n}}
         sweep = {"per_tau": sweep, "fit": fit}
 
-    # ---- CPU baseline: the oracle on a bounded sample of step 0 (empty mask) ----
+    # ---- CPU baseline: the oracle's calls on the sampled rows of the timed trajectory ----
     cpu = None
-    if not args.no_cpu:
-        import numpy as np
-        from oracle import oracle
-        nth = cpu_threads()
-        nrows = args.cpu_rows or 6 * nth
-        q0, k0, v0 = step0
-        rng = np.random.default_rng(0)
-        rows = np.sort(rng.choice(wl.rows, size=min(nrows, wl.rows), replace=False)).astype(np.int64)
-        qc, kc, vc = q0.cpu(), k0.cpu(), v0.cpu()
-        t0c = time.perf_counter()
-        res = oracle.fwd(qc, kc, vc, wl.tile_m, wl.tile_n, tau_at(0), scale, rows=rows, nthreads=nth)
-        tc = time.perf_counter() - t0c
-        tq = wl.tq
-        rf = 0.0
-        for r in rows:
-            qt = int(r % tq)
-            vr = min(wl.tile_m, wl.seqlen - qt * wl.tile_m)
-            rf += 4.0 * wl.head_dim * vr * wl.seqlen
-        cpu = {"value": round(rf / tc / 1e12, 6), "unit": "TFLOP/s", "cores": res["nthreads"], "kind": "oracle",
-               "sample": "%d of %d q-tile rows of step 0 (empty mask, every tile live), fp64, %.1f s on %d threads "
-                         "of %s" % (len(rows), wl.rows, tc, res["nthreads"], cpu_model())}
-        del qc, kc, vc
+    verification = None
+    if chk is not None:
+        cpu = {"value": round(chk.flops / chk.seconds / 1e12, 6), "unit": "TFLOP/s",
+               "cores": min(chk.threads, len(chk.rows)), "kind": "oracle",
+               "sample": "%d of %d q-tile rows (%d heads, incl. the last head's last partial q-tile), carried by "
+                         "the oracle through steps 0..%d of the trajectory from an empty mask; live tiles only, "
+                         "fp64, %.1f s on %d threads of %s"
+                         % (len(chk.rows), wl.rows, len({int(r // wl.tq) for r in chk.rows}), W + K - 1,
+                            chk.seconds, min(chk.threads, len(chk.rows)), cpu_model())}
+        verification = {
+            "rule": "outputs max-abs <= %g, lse <= %g, masks bit-exact off a 1e-3 band around tau (counted as "
+                    "near_tau); rows compared where the carried masks agree" % (
+                        pa.TOL_OUT[out.dtype], pa.TOL_LSE[out.dtype]),
+            "max_abs_out": max((c["max_abs_out"] for c in checks), default=None),
+            "max_lse": max((c["max_lse"] for c in checks), default=None),
+            "mask_mismatch": sum(c["mask_mismatch"] for c in checks),
+            "near_tau": sum(c["near_tau"] for c in checks),
+            "diverged_rows": sum(c["diverged_rows"] for c in checks),
+            "within_bars": all(c["within_bars"] for c in checks),
+            "sweep_masks_equal_timed_run": sweep_same_as_timed if sweep else None,
+            "steps": checks}
 
     variants = dense_variants(torch, la) if args.dense_variants else None
 
@@ -485,6 +643,7 @@ def main():
                      if bf16 else "fwd_fp32_kernel",
                      "kernel_source_sha256_16": src_hash},
         "cpu_baseline": cpu,
+        "verification": verification,
         "tau_sweep": sweep,
         "dense_variants": variants,
     }

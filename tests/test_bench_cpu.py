@@ -101,3 +101,75 @@ def test_every_workload_gets_to_its_first_gpu_call():
                             "--warmup", "0", "--sweep-steps", "0", "--no-cpu"], env=env, capture_output=True,
                            text=True, timeout=300)
         assert "[bench] workload %s:" % name in p.stderr, (name, p.stderr[-1500:])
+
+
+def test_rows_live_flops_brute_force():
+    wl = configs.scaled(configs.C4, (3, 10, 30), heads=3, batch=2)
+    rows = np.array([0, wl.tq - 1, wl.rows - 1], np.int64)
+    for density in (0.0, 0.5):
+        mw = synth.random_mask(wl.rows, wl.tk, density, seed=9).numpy().view(np.uint32)
+        bits = _bits(torch.from_numpy(mw.view(np.int32)).reshape(-1), wl)
+        want = 0.0
+        for r in rows:
+            qt = r % wl.tq
+            nr = min(wl.seqlen, (qt + 1) * wl.tile_m) - qt * wl.tile_m
+            for kt in range(wl.tk):
+                if not bits[r, kt]:
+                    want += 4.0 * wl.head_dim * nr * (min(wl.seqlen, (kt + 1) * wl.tile_n) - kt * wl.tile_n)
+        assert bench.rows_live_flops(mw[rows], rows, wl) == want
+
+
+def test_oracle_check_compares_what_it_should():
+    """The benchmark's check of timed steps: GPU results equal to the oracle's
+    own (made here from the oracle's numbers, as a stand-in) are within the bars
+    with every row compared; a row whose carried mask differs from the oracle's
+    is counted as diverged and left out; a wrong output or mark is flagged."""
+    import math
+    wl = configs.scaled(configs.C4, (6, 10, 16), heads=2, batch=2)         # N 960: Tq = Tk = 8
+    q, k, v = synth.Trajectory(wl, "cpu").tensors()
+    rows = np.array([0, 3, wl.rows - 1, wl.rows - 2], np.int64)
+    chk = bench.OracleCheck(wl, 1.0 / math.sqrt(wl.head_dim), rows, 2)
+    chk.step("t", 0, q, k, v, 0.0, keep=True)
+    chk.step("t", 1, q, k, v, 0.0, keep=True)
+    res, rm = chk.results[("t", 1)]
+    assert chk.flops > 0 and chk.seconds > 0
+    B, N, H, D, BM, W = wl.batch, wl.seqlen, wl.heads, wl.head_dim, wl.tile_m, wl.mask_words
+    out = torch.zeros(B, N, H, D, dtype=torch.bfloat16)
+    lse = torch.zeros(B, H, N)
+    m_in = torch.zeros(wl.rows * W, dtype=torch.int32)
+    m_out = torch.zeros(wl.rows * W, dtype=torch.int32)
+    for i, r in enumerate(rows):
+        b, h, qt = int(r // (wl.tq * H)), int((r // wl.tq) % H), int(r % wl.tq)
+        nr = min(BM, N - qt * BM)
+        out[b, qt * BM:qt * BM + nr, h] = torch.from_numpy(res["out"][i][:nr]).to(torch.bfloat16)
+        lse[b, h, qt * BM:qt * BM + nr] = torch.from_numpy(res["lse"][i][:nr]).float()
+        m_in.view(-1, W)[r] = torch.from_numpy(rm[i].view(np.int32))
+        m_out.view(-1, W)[r] = torch.from_numpy(res["mask_out"][i].view(np.int32))
+    c = chk.compare("t", 1, 0.0, out, lse, m_in, m_out)
+    assert c["within_bars"] and c["rows_compared"] == 4 and c["diverged_rows"] == 0, c
+    assert rm.any(), "the carried mask is empty: the test would not see it compared"
+    # a diverged carried mask: that row is left out
+    m_in2 = m_in.clone()
+    m_in2.view(-1, W)[rows[0], 0] ^= 1 << 2
+    c = chk.compare("t", 1, 0.0, out, lse, m_in2, m_out)
+    assert c["diverged_rows"] == 1 and c["rows_compared"] == 3 and c["within_bars"], c
+    # a wrong output and a wrong mark are flagged
+    out2 = out.clone()
+    out2[0, 5, 0, 3] += 0.5
+    assert not chk.compare("t", 1, 0.0, out2, lse, m_in, m_out)["within_bars"]
+    m_out2 = m_out.clone()
+    margins = res["margin"][1]
+    kt = int(np.nanargmax(np.where(np.isfinite(margins), np.abs(margins), -1)))
+    m_out2.view(-1, W)[rows[1], kt // 32] ^= 1 << (kt % 32)
+    c = chk.compare("t", 1, 0.0, out, lse, m_in, m_out2)
+    assert c["mask_mismatch"] == 1 and not c["within_bars"], c
+    # a step without mask_in / mask_out (the dense check) compares outputs only
+    chk.step("d", 0, q, k, v, -math.inf, keep=True)
+    res, _ = chk.results[("d", 0)]
+    for i, r in enumerate(rows):
+        b, h, qt = int(r // (wl.tq * H)), int((r // wl.tq) % H), int(r % wl.tq)
+        nr = min(BM, N - qt * BM)
+        out[b, qt * BM:qt * BM + nr, h] = torch.from_numpy(res["out"][i][:nr]).to(torch.bfloat16)
+        lse[b, h, qt * BM:qt * BM + nr] = torch.from_numpy(res["lse"][i][:nr]).float()
+    c = chk.compare("d", 0, -math.inf, out, lse, None, None)
+    assert c["within_bars"] and c["rows_compared"] == 4 and c["tau"] is None, c

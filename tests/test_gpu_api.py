@@ -1,8 +1,9 @@
 """The per-layer class mirroring the README's Python API, on the GPU, against
 the oracle step by step: the carried Skip-Mask, set_threshold,
 enable_skip_optimization(False) (plain attention, mask untouched) and
-reset_skip_state."""
+reset_skip_state; and the skip state's checkpoint round trip."""
 
+import io
 import math
 import sys
 
@@ -53,7 +54,10 @@ def test_layer_class_against_the_oracle():
         o_ref, _ = oracle.unpack_rows(orc, wl.batch, wl.seqlen, wl.heads, wl.tile_m)
         assert float(np.abs(out.cpu().double().numpy() - o_ref).max()) <= pa.TOL_OUT[torch.bfloat16]
         near_tau_ok(gpu_mask(), orc, -3.0)
-        mask = gpu_mask().copy()            # follow the GPU's mask (equal off near-tau ties)
+        # the oracle carries its own marks; the layer's state is set to them, so
+        # both start the next step from one mask even after a near-tau tie
+        mask = orc["mask_out"].copy()
+        attn.mask.copy_(torch.from_numpy(mask.view(np.int32).reshape(-1)).cuda())
     assert mask.any(), "nothing marked: the test would not see the mask carried"
 
     # skipping off: plain attention, mask untouched
@@ -85,3 +89,55 @@ def test_layer_class_against_the_oracle():
     o_ref, _ = oracle.unpack_rows(orc, wl.batch, wl.seqlen, wl.heads, wl.tile_m)
     assert float(np.abs(out.cpu().double().numpy() - o_ref).max()) <= pa.TOL_OUT[torch.bfloat16]
     near_tau_ok(gpu_mask(), orc, -1.0)
+
+
+@pytest.mark.parametrize("use_skiplist", [False, True], ids=["bitmask", "skiplist"])
+def test_checkpoint_round_trip_of_the_skip_state(use_skiplist):
+    """The skip state is the layer's only state across denoising steps (README
+    Python API: one instance per layer, reset_skip_state).  On the 4,096-token,
+    12-head trajectory at tau = -3: 10 steps in one layer object equal 5 steps,
+    the state saved to the host and through torch.save / torch.load
+    (weights_only), restored into a new layer object, and 5 more steps -- bit
+    for bit in outputs, lse and the mask after every step."""
+    wl = configs.C2
+    tr = synth.Trajectory(wl, "cuda")
+    inputs = []
+    for t in range(10):
+        if t:
+            tr.advance()
+        inputs.append(tr.tensors())
+    del tr
+    kw = dict(threshold=-3.0, tile_m=wl.tile_m, tile_n=wl.tile_n, use_skiplist=use_skiplist)
+    ref = la.LiteAttention(**kw)
+    assert ref.skip_state() is None
+    want = []
+    for q, k, v in inputs:
+        o, l = ref(q, k, v, return_softmax_lse=True)
+        want.append((o, l, ref.mask.clone()))
+    a = la.LiteAttention(**kw)
+    got = []
+    for q, k, v in inputs[:5]:
+        o, l = a(q, k, v, return_softmax_lse=True)
+        got.append((o, l, a.mask.clone()))
+    state = a.skip_state()
+    assert state["mask"].device.type == "cpu" and state["mask"].any()
+    buf = io.BytesIO()
+    torch.save(state, buf)
+    buf.seek(0)
+    state = torch.load(buf, weights_only=True)
+    del a
+    b = la.LiteAttention(**kw)
+    b.load_skip_state(state)
+    for q, k, v in inputs[5:]:
+        o, l = b(q, k, v, return_softmax_lse=True)
+        got.append((o, l, b.mask.clone()))
+    torch.cuda.synchronize()
+    for t, (w, g) in enumerate(zip(want, got)):
+        assert torch.equal(w[0], g[0]) and torch.equal(w[1], g[1]), "step %d output/lse" % t
+        assert torch.equal(w[2], g[2]), "step %d mask" % t
+    sp = [float((w[2] != 0).float().mean()) for w in want]
+    assert sp[9] >= sp[4] > 0, sp
+    # clearing the state starts again from an empty mask
+    b.load_skip_state(None)
+    o, l = b(*inputs[0], return_softmax_lse=True)
+    assert torch.equal(o, want[0][0]) and torch.equal(b.mask, want[0][2])
