@@ -43,7 +43,9 @@
 //   instructions.  Four LDS stages (128 KB at head_dim 128) and a prefetch
 //   distance of two steps: while step u is computed (its K read by both
 //   halves in step u, its V by both halves in step u + 1), step u + 1 is in
-//   flight and A's waves issue step u + 2 among their QK^T MFMAs.  Each
+//   flight and A's waves issue step u + 2 among their QK^T MFMAs.  The four
+//   stages' K share one LDS array and their V another, so each LDS read
+//   address is a per-lane register computed once plus an immediate.  Each
 //   load's source is a buffer resource (base, byte range) built in scalar
 //   registers per 16 or 32 key rows, so addresses cost no vector
 //   instructions, and rows past the end of the sequence read as zeros through
@@ -130,8 +132,8 @@ struct Step {
     int key0;  // first key
 };
 
-// One 16-byte direct-to-LDS load: each lane's `src`, into `dst` + 16 * lane
-// (dst is wave-uniform).
+// One 16-byte direct-to-LDS load: each lane's source, into LDS address
+// l + 16 * lane (l is wave-uniform; it goes through M0).
 // The source is a raw buffer resource (base, byte range) plus this lane's byte
 // offset: an offset at or past the range reads zeros, which is how rows past
 // the end of the sequence are handled.  Issued from an asm block: the compiler
@@ -139,9 +141,8 @@ struct Step {
 // kernel waits for them explicitly (vmcnt) before the barriers that publish a
 // stage and before it exits.  The leading s_nop covers the wait states an
 // M0 or SGPR write needs before a buffer load reads it.
-__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t off, char *dst)
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t off, uint32_t l)
 {
-    const uint32_t l = (uint32_t)(size_t)LDS_VOID(dst);
     asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(l));
 }
 
@@ -170,7 +171,8 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const char *base, uint32_t bytes)
     return r;
 }
 
-// LDS layout of one 64-key step.  K and V arrive by direct-to-LDS loads
+// LDS layout of one 64-key step (a stage: CH chunks of K in kbuf, CH chunks
+// of V in vbuf).  K and V arrive by direct-to-LDS loads
 // (buffer_load_dwordx4 ... lds): each wave instruction writes 64 consecutive
 // 16-byte chunks, lane i to chunk i, so the layout is any permutation of the
 // step's chunks -- chosen per lane by the byte offset it loads.
@@ -185,7 +187,6 @@ template <int D>
 struct Geo {
     static constexpr int CPR = D / 8;       // 16-byte chunks per row
     static constexpr int CH = HK * CPR;     // chunks of a K (or V) step
-    static constexpr int STAGE = 2 * CH;    // K then V, in chunks
     static constexpr int IPA = CH / 64 / 4; // DMA instructions per A-wave, per tensor
     static constexpr int RPI = 256 / CPR;   // key rows covered by one instruction round of the 4 A-waves
     static_assert(CH % (64 * 4) == 0, "unsupported step geometry");
@@ -210,12 +211,11 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
 {
     using G = Geo<D>;
     constexpr int SPT = BN / HK;  // steps per k-tile
-    // Four distinct LDS objects, one per pipeline stage: the compiler can then
-    // tell a stage being read from the stages being filled by DMA.
-    __shared__ u32x4 stage0[G::STAGE];
-    __shared__ u32x4 stage1[G::STAGE];
-    __shared__ u32x4 stage2[G::STAGE];
-    __shared__ u32x4 stage3[G::STAGE];
+    // The four pipeline stages: K of all four in one array, V in another, so
+    // that every LDS read is a per-lane address register computed once plus
+    // an immediate offset (stage, key block), which stays below 64 KB.
+    __shared__ u32x4 kbuf[4 * G::CH];
+    __shared__ u32x4 vbuf[4 * G::CH];
     __shared__ uint32_t keep[2][MAXW];
     __shared__ uint32_t wlive[2][MAXW];   // live tiles of A and B, one bit per k-tile
     __shared__ int32_t wcnt[MAXW];        // tiles of the union per mask word
@@ -282,17 +282,18 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     // rows of that block that exist, so rows past the end of the sequence read
     // as zeros (their logits are set to -inf before use) and no address leaves
     // the tensors.  All of it is scalar arithmetic.
+    const uint32_t m0_k = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)LDS_VOID(kbuf) + wq * 64 * 16);
+    const uint32_t m0_v = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)LDS_VOID(vbuf) + wq * 64 * 16);
     const uint32_t koff = (uint32_t)(kr0 * rs2 + kc0);
     const uint32_t voff = (uint32_t)(vr0 * rs2 + vc0);
     struct DmaPlan {
         const char *kb, *vb;
-        char *kdst, *vdst;
+        int st;
         int bytes;  // bytes of the step's rows that exist: min(Nk - key0, HK) rows
     };
-    auto plan_step = [&](int key0, u32x4 *dst) __attribute__((always_inline)) {
+    auto plan_step = [&](int key0, int st) __attribute__((always_inline)) {
         DmaPlan d;
-        d.kdst = (char *)dst + wq * 64 * 16;
-        d.vdst = d.kdst + G::CH * 16;
+        d.st = st;
         d.kb = Kb + (int64_t)key0 * rs2;
         d.vb = Vb + (int64_t)key0 * rs2;
         d.bytes = min(Nk - key0, HK) * rs2;
@@ -305,8 +306,14 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         x &= ~(x >> 31);
         const uint32_t bytes = (uint32_t)min(x, G::RPI * rs2);
         const int64_t blk = (int64_t)i * G::RPI * rs2;
-        dma16(buffer_rsrc(d.kb + blk, bytes), koff, d.kdst + i * 4 * 64 * 16);
-        dma16(buffer_rsrc(d.vb + blk, bytes), voff, d.vdst + i * 4 * 64 * 16);
+        // LDS destinations: this wave's base, made opaque so that the compiler
+        // adds the stage/instruction offset here instead of keeping one
+        // precomputed scalar per (stage, instruction) live across the loop
+        uint32_t kb0 = m0_k, vb0 = m0_v;
+        asm volatile("" : "+s"(kb0), "+s"(vb0));
+        const uint32_t o = (uint32_t)(d.st * G::CH * 16 + i * 4 * 64 * 16);
+        dma16(buffer_rsrc(d.kb + blk, bytes), koff, kb0 + o);
+        dma16(buffer_rsrc(d.vb + blk, bytes), voff, vb0 + o);
     };
 
     // This lane's slot as a source of the transposed V read: key row 8g + a of
@@ -321,6 +328,20 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     const int vtr_row = 8 * g + (ts >> 2);
     const int vtr_col = (16 * (tb & 1) + 8 * ((lane >> 4) & 1) + 4 * (tb >> 1)) * 2;  // bytes in a 64-B segment
     const int vtr_seg = v_swz<D>(vtr_row) / 4;                                       // segment XOR
+    // Per-lane LDS read addresses, computed once: V^T reads of head-dim block
+    // eb, and K reads of head-dim step ds; stage, key block and half offsets
+    // are immediates of the reads.
+    uint32_t vaddr[D / 32], kaddr[D / 16];
+#pragma unroll
+    for (int eb = 0; eb < D / 32; ++eb) {
+        vaddr[eb] = (uint32_t)(size_t)LDS_VOID(vbuf) + vtr_row * G::CPR * 16 + vtr_col + ((eb ^ vtr_seg) * 64);
+        asm volatile("" : "+v"(vaddr[eb]));
+    }
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+        kaddr[ds] = (uint32_t)(size_t)LDS_VOID(kbuf) + (lq * G::CPR + ((2 * ds) ^ (g ^ k_swz<D>(lq)))) * 16;
+        asm volatile("" : "+v"(kaddr[ds]));
+    }
 
     f32x16 O[D / 32];
 #pragma unroll
@@ -437,19 +458,17 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     // ---- O^T += V^T P^T over one step (V in LDS stage vst) ----
     // MFMA order ks-major over the D/32 independent accumulators; each
     // transposed V read is issued AHEAD MFMAs before its use.
-    auto pv_gemm = [&](const u32x4 *vst) __attribute__((always_inline)) {
+    auto pv_gemm = [&](int vs) __attribute__((always_inline)) {
         constexpr int NEB = D / 32, NM = NEB * (HK / 16);
-        // lane offsets recomputed here, not kept live across the loop
-        int vl = vtr_row * G::CPR * 16 + vtr_col, vsg = vtr_seg;
-        asm volatile("" : "+v"(vl), "+v"(vsg));
-        const char *Vs = (const char *)(vst + G::CH) + vl;
         // MFMA m = ks*NEB + eb; its operand is read AHEAD MFMAs earlier
         s16x8 vf[NM];
         auto rd = [&](int m) __attribute__((always_inline)) {
             const int ks = m / NEB, eb = m % NEB;
-            const char *va = Vs + 16 * ks * G::CPR * 16 + ((eb ^ vsg) * 64);
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_S16X4(va + 4 * G::CPR * 16));
+            typedef __attribute__((address_space(3))) char lchar;
+            lchar *va = (lchar *)(size_t)vaddr[eb] + vs * G::CH * 16 + 16 * ks * G::CPR * 16;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)va);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(va + 4 * G::CPR * 16));
             vf[m] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         };
 #pragma unroll
@@ -475,24 +494,21 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     // MFMA order ds-major over the two 32-key blocks; one K read per MFMA,
     // issued AHEAD MFMAs before its use.  With WD the loads of the next step
     // (`dma`) go out one per two MFMAs.
-    auto s_gemm = [&](const u32x4 *kst, const DmaPlan &dma, auto with_dma) __attribute__((always_inline)) {
+    auto s_gemm = [&](int ks_, const DmaPlan &dma, auto with_dma) __attribute__((always_inline)) {
         constexpr bool WD = decltype(with_dma)::value;
         constexpr int NDS = D / 16, NM = (HK / 32) * NDS;
         static_assert(NM == 4 * G::IPA, "one load pair per four MFMAs");
         // Row kb*32 + lq, chunk (2*ds + g) ^ k_swz(row) = 2*ds ^ kc: the swizzle
-        // depends on the row only through lq.  Lane offsets recomputed here.
-        int kl = lq * G::CPR, kc = g ^ k_swz<D>(lq);
-        asm volatile("" : "+v"(kl), "+v"(kc));
-#pragma unroll
-        for (int kb = 0; kb < HK / 32; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                S[kb][v] = 0.f;
-        // MFMA m = ds*2 + kb; its K fragment is read AHEAD MFMAs earlier
+        // depends on the row only through lq (kaddr).
+        // MFMA m = ds*2 + kb; its K fragment is read AHEAD MFMAs earlier.
+        // The first MFMA of each accumulator takes a zero C operand (an inline
+        // constant), so S needs no clearing moves.
         u32x4 kf[NM];
         auto rd = [&](int m) __attribute__((always_inline)) {
             const int ds = m >> 1, kb = m & 1;
-            kf[m] = kst[kb * 32 * G::CPR + kl + ((2 * ds) ^ kc)];
+            typedef __attribute__((address_space(3))) u32x4 lvec;
+            kf[m] = *(lvec *)((__attribute__((address_space(3))) char *)(size_t)kaddr[ds] +
+                              (ks_ * G::CH + kb * 32 * G::CPR) * 16);
         };
 #pragma unroll
         for (int m = 0; m < AHEAD; ++m)
@@ -501,8 +517,9 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         for (int m = 0; m < NM; ++m) {
             if (m + AHEAD < NM)
                 rd(m + AHEAD);
+            const f32x16 zero = {};
             S[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[m]), qf[m >> 1],
-                                                               S[m & 1], 0, 0, 0);
+                                                               m < 2 ? zero : S[m & 1], 0, 0, 0);
             // one (K, V) pair per four MFMAs: NM = 4 * IPA for both head dims
             if (WD && (m & 3) == 3)
                 issue_dma(dma, m >> 2);
@@ -586,7 +603,7 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     constexpr int VM_KEEP = 2 * G::IPA;
     constexpr int WAIT_KEEP = (VM_KEEP & 15) | (7 << 4) | (15 << 8) | ((VM_KEEP >> 4) << 14);  // vmcnt only
     constexpr int WAIT_ALL = (7 << 4) | (15 << 8);  // vmcnt(0) only
-    auto load_step = [&](const Step &s, u32x4 *dst) __attribute__((always_inline)) {
+    auto load_step = [&](const Step &s, int dst) __attribute__((always_inline)) {
         if (Nk <= 0)
             return;  // no key rows at all
         const DmaPlan d = plan_step(loadable(s) ? s.key0 : Nk, dst);
@@ -600,8 +617,8 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     Step sn = gen();          // step u + 1
     Step sn2 = gen();         // step u + 2
     if (half == 0) {
-        load_step(sc, stage0);
-        load_step(sn, stage1);
+        load_step(sc, 0);
+        load_step(sn, 1);
         __builtin_amdgcn_s_waitcnt(WAIT_KEEP);  // step 0 has landed
     }
     __syncthreads();
@@ -616,7 +633,7 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         constexpr int HF = decltype(half_tag)::value;
         // MFMA part: PV of step u - 1, then QK^T of step u; the A-waves load
         // step u + 2 meanwhile (spread over the QK^T MFMAs).
-        auto mfma_part = [&](const u32x4 *vst, const u32x4 *kst, u32x4 *lst) __attribute__((always_inline)) {
+        auto mfma_part = [&](int vst, int kst, int lst) __attribute__((always_inline)) {
             if (act(sp))
                 pv_gemm(vst);
             if (HF == 0) {
@@ -633,9 +650,7 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
             constexpr int ST = decltype(stage_tag)::value;
             if (sc.kt < 0 && sp.kt < 0)
                 return false;
-            u32x4 *const kst = ST == 0 ? stage0 : (ST == 1 ? stage1 : (ST == 2 ? stage2 : stage3));
-            u32x4 *const lst = ST == 0 ? stage2 : (ST == 1 ? stage3 : (ST == 2 ? stage0 : stage1));
-            u32x4 *const vst = ST == 0 ? stage3 : (ST == 1 ? stage0 : (ST == 2 ? stage1 : stage2));
+            constexpr int kst = ST, lst = (ST + 2) & 3, vst = (ST + 3) & 3;
             // A: MFMAs, then softmax; B: softmax, then MFMAs.  No barrier in
             // between: the opposite orders alone keep one wave of each SIMD on
             // the matrix core while the other is on the vector ALU.
