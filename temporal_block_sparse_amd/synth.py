@@ -109,9 +109,11 @@ class Trajectory:
                                            device=self.device), alpha=wl.drift_v)
 
     def tensors(self):
-        """(q, k, v) in the workload's storage dtype, contiguous BSHD."""
+        """(q, k, v) in the workload's storage dtype, contiguous BSHD: new
+        tensors, which later steps of drift do not change (the fp32 state is
+        copied too, not returned by reference)."""
         dt = torch.bfloat16 if self.wl.dtype == "bf16" else torch.float32
-        return (self.q.to(dt).contiguous(), self.k.to(dt).contiguous(), self.v.to(dt).contiguous())
+        return tuple(x.to(dt, copy=True).contiguous() for x in (self.q, self.k, self.v))
 
 
 def random_qkv(batch, seqlen, heads, head_dim, dtype=torch.float32, seed=0, scale=1.0, device="cpu"):

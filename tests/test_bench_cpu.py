@@ -173,3 +173,16 @@ def test_oracle_check_compares_what_it_should():
         lse[b, h, qt * BM:qt * BM + nr] = torch.from_numpy(res["lse"][i][:nr]).float()
     c = chk.compare("d", 0, -math.inf, out, lse, None, None)
     assert c["within_bars"] and c["rows_compared"] == 4 and c["tau"] is None, c
+
+
+def test_trajectory_tensors_are_snapshots():
+    """A step's tensors must not change when the trajectory drifts on: the
+    benchmark keeps the timed steps' inputs while it advances (the fp32
+    workload's state was once returned by reference)."""
+    for wl in (configs.C1, configs.scaled(configs.C2, (2, 4, 8), heads=1)):
+        tr = synth.Trajectory(wl, "cpu")
+        q, k, v = tr.tensors()
+        q0 = q.clone()
+        tr.advance()
+        assert torch.equal(q, q0)
+        assert not torch.equal(tr.tensors()[0], q0)
