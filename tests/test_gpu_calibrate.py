@@ -5,8 +5,10 @@ seeded drifting inputs.
 The calibration compares a candidate's relative output error with the step's
 budget; bf16 outputs move that error by about 2^-9 relative, so a step whose
 oracle error for the chosen or the next candidate lies within 3e-3 of the
-budget is a tie: from there on either choice is accepted and the trajectories
-are no longer compared."""
+budget is a tie, where either choice is accepted.  The end-to-end test stops
+comparing at the first tie (the two trajectories may part there); the
+step-wise test starts every GPU step from the oracle's carried mask and so
+compares every step."""
 
 import math
 import sys
@@ -97,3 +99,69 @@ def test_calibration_matches_the_oracle(use_skiplist):
         log("  tie at step %d: stop comparing" % t)
         break
     assert any(g["sparsity"] > 0 for g in gpu)
+
+
+def _oracle_error(q, k, v, wl, scale, tau, mask_in):
+    """The oracle's relative output error of candidate tau from mask_in (fp64)."""
+    B, N, H, _ = q.shape
+    dense = oracle.fwd(q, k, v, wl.tile_m, wl.tile_n, -math.inf, scale)
+    od, _ = oracle.unpack_rows(dense, B, N, H, wl.tile_m)
+    m2 = oracle.fwd(q, k, v, wl.tile_m, wl.tile_n, tau, scale, mask_in=mask_in)
+    o2, _ = oracle.unpack_rows(oracle.fwd(q, k, v, wl.tile_m, wl.tile_n, -math.inf, scale, mask_in=m2["mask_out"]),
+                               B, N, H, wl.tile_m)
+    return float(np.sqrt(((o2 - od) ** 2).sum() / (od ** 2).sum())), m2
+
+
+@pytest.mark.parametrize("use_skiplist", [False, True])
+def test_calibration_every_step_from_the_oracles_mask(use_skiplist):
+    """Every step of an 8-step calibrated trajectory, not only the steps up to
+    the first tie: each GPU step starts from the mask the oracle's own
+    calibration carried into that step (a GPU input taken from the oracle), so
+    one tie does not end the comparison.  The GPU must choose the oracle's
+    threshold -- or, at a tie (the oracle's error for the chosen or the next
+    larger candidate within TIE of the budget), a neighbour of it -- and, with
+    the same threshold, the oracle's marks (bit-exact off the 1e-3 band of tau)
+    and its error to within TIE."""
+    wl = configs.scaled(configs.C2, (8, 8, 8), heads=2, batch=1, steps=8)     # 512 tokens, d = 64, tile 128x64
+    tr = synth.Trajectory(wl, "cpu")
+    steps = []
+    for t in range(wl.steps):
+        if t:
+            tr.advance()
+        steps.append(tr.tensors())
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    taus = [0.0, -1.0, -2.0, -3.0, -5.0, -8.0]
+    base, ratio = 0.03, 0.5                                  # budgets ramp over the first 4 steps
+    orc = oracle.calibrate(steps, wl.tile_m, wl.tile_n, scale, base, taus, early_step_ratio=ratio)
+    mult = calibrate.error_budgets(wl.steps, ratio)
+    cands = sorted(taus, reverse=True) + [-math.inf]
+    dev = torch.device("cuda")
+    agree = 0
+    for t, o in enumerate(orc):
+        mask_in = orc[t - 1]["mask"] if t else None
+        mi = None if mask_in is None else torch.from_numpy(np.ascontiguousarray(mask_in).view(np.int32).reshape(-1)).to(dev)
+        q, k, v = steps[t]
+        assert base * mult[t] == o["budget"]
+        tau, err, m = calibrate.calibrate_step(q.to(dev), k.to(dev), v.to(dev), mi, wl.tile_m, wl.tile_n,
+                                               o["budget"], taus, softmax_scale=scale, use_skiplist=use_skiplist)
+        log("  step %d oracle tau %g err %.4g budget %.4g | gpu tau %g err %.4g"
+            % (t, o["tau"], o["error"], o["budget"], tau, err))
+        if tau == o["tau"]:
+            agree += 1
+            assert abs(err - o["error"]) <= TIE
+            mg = m.cpu().numpy().view(np.uint32).reshape(o["mask"].shape)
+            ref = oracle.fwd(q, k, v, wl.tile_m, wl.tile_n, tau, scale, mask_in=mask_in)
+            diff = np.unpackbits((mg ^ ref["mask_out"]).view(np.uint8), bitorder="little").reshape(mg.shape[0], -1)
+            for r, kt in zip(*np.nonzero(diff)):
+                assert abs(ref["margin"][r, kt] - tau) <= 1e-3, "step %d: mark differs at row %d tile %d" % (t, r, kt)
+            continue
+        # a different choice is accepted only at a tie
+        i = cands.index(o["tau"])
+        near = abs(o["error"] - o["budget"]) <= TIE
+        if not near and i > 0:
+            e_next, _ = _oracle_error(q, k, v, wl, scale, cands[i - 1], mask_in)
+            near = abs(e_next - o["budget"]) <= TIE
+        assert near, "step %d: gpu tau %g vs oracle tau %g away from a tie" % (t, tau, o["tau"])
+        log("  tie at step %d" % t)
+    assert agree >= wl.steps - 2, "only %d of %d steps agree" % (agree, wl.steps)
+    assert any(o["sparsity"] > 0 for o in orc)
