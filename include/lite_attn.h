@@ -65,7 +65,10 @@
 extern "C" {
 #endif
 
-#define LITE_ATTN_ABI_VERSION 2
+#define LITE_ATTN_ABI_VERSION 3
+
+/* uint32 words of the forward's schedule counters (lite_attn_fwd, sched). */
+#define LITE_ATTN_SCHED_WORDS 2
 
 typedef enum {
     LITE_BF16 = 0, /* bf16 q, k, v, out; fp32 accumulation */
@@ -163,6 +166,20 @@ size_t lite_attn_skiplist_len(const lite_attn_desc *desc);
  *             for merging partial attentions); -inf when the row has no live
  *             tile.
  *   ranges    host, or NULL for none: must-do / must-skip key ranges.
+ *   sched     device, LITE_ATTN_SCHED_WORDS uint32, 4-byte aligned, or NULL:
+ *             schedule counters of the bf16 forward (ignored for LITE_FP32).
+ *             With counters, one persistent workgroup per compute unit takes
+ *             the q-tile pairs in order from an atomic ticket, which keeps
+ *             every compute unit busy when the pairs' costs differ (sparse
+ *             masks); NULL launches one workgroup per pair.  Results are the
+ *             same bit for bit either way.  The words must be zero before the
+ *             first call that uses them; every call leaves them zero again
+ *             (the last workgroup resets them, no memset), so a buffer zeroed
+ *             once serves any number of calls, also inside HIP graph capture.
+ *             Calls that may run at the same time (on different streams, or
+ *             replays of graphs that captured it) must not share one buffer;
+ *             calls on one stream never overlap.  Owned by the caller; may not
+ *             overlap any other buffer of the call (LITE_ERR_ALIAS).
  *   stream    hipStream_t.
  * With the environment variable LITE_ATTENTION_VERBOSE set to anything other
  * than "FALSE" ([README] debug flags), each call that passes validation prints
@@ -171,7 +188,7 @@ size_t lite_attn_skiplist_len(const lite_attn_desc *desc);
 int lite_attn_fwd(const lite_attn_desc *desc, const void *q, const void *k, const void *v,
                   const uint32_t *mask_in, uint32_t *mask_out, const int32_t *skiplist,
                   float tau, float softmax_scale, void *out, float *lse, const lite_attn_ranges *ranges,
-                  void *stream);
+                  uint32_t *sched, void *stream);
 
 /*
  * lite_attn_build_skiplist -- compact each row of a Skip-Mask into its

@@ -19,6 +19,16 @@
 //   visits, so each q-tile sees exactly its own live tiles in its own order:
 //   decisions and outputs are those of a one-q-tile kernel.  Both q-tiles
 //   read the same K/V from LDS, so one copy of a step serves 256 queries.
+// * Schedule: with schedule counters (two words in device memory), the grid
+//   is one persistent workgroup per compute unit, and each takes the next
+//   q-tile pair from an atomic ticket counter when it finishes one.  The
+//   hardware hands workgroups to the XCDs round-robin and to the CUs of an XCD
+//   in order; once the pairs' costs differ (sparse masks), that left whole
+//   XCDs idle at the end of a launch and each CU idle between workgroups.
+//   Tickets are taken in pair order, so all CUs still work on the q-tiles of
+//   one or two heads at a time.  The last workgroup to finish resets the
+//   counters, so they are zero again for the next launch without a memset.
+//   Without counters, one workgroup per pair, in order.
 // * Ping-pong: within a step, A's waves first run their MFMAs (PV of the
 //   previous step, then QK^T of this one) and then the softmax of this step;
 //   B's waves run the softmax of the previous step first and their MFMAs
@@ -75,6 +85,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 namespace lite_attn {
@@ -207,7 +218,7 @@ __device__ __forceinline__ int v_swz(int r)
 
 template <int D, int BN, bool LIST>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
-fwd_bf16_kernel(FwdParams p, float c2, float tau2)
+fwd_bf16_kernel(FwdParams p, float c2, float tau2, int npairs)
 {
     using G = Geo<D>;
     constexpr int SPT = BN / HK;  // steps per k-tile
@@ -221,46 +232,15 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     __shared__ int32_t wcnt[MAXW];        // tiles of the union per mask word
     __shared__ uint16_t walk[MAXW * 32];  // the union walk: k-tile | A visits << 12 | B visits << 13
     __shared__ int32_t nwalk;
-
+    __shared__ int s_pair;
+    // Lane and wave constants, and the LDS and global byte offsets built from
+    // them, are computed once for all pairs.
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
     const int half = wave >> 2;                                 // 0: q-tile A, 1: q-tile B
     const int wq = wave & 3;                                    // 32-query block in the q-tile
     const int g = lane >> 5, lq = lane & 31;
-    const int Nq = p.Nq, Nk = p.Nk, H = p.H, Tq = p.Tq, Tk = p.Tk, W = p.W;
-    const int Tq2 = (Tq + 1) >> 1;
-    const int pq = (int)(blockIdx.x % Tq2);
-    const int64_t bh = blockIdx.x / Tq2;
-    const int h = (int)(bh % H), b = (int)(bh / H);
-    const bool has_b = 2 * pq + 1 < Tq;
-    const int64_t row_a = bh * Tq + 2 * pq;  // q-tile B is row_a + 1
-    const int qt = 2 * pq + half;            // this wave's q-tile
-    const int rs = H * D;                    // token stride (elements)
-    const int rs2 = rs * 2;                  // token stride (bytes)
-    const int64_t qbase = (int64_t)b * p.q_sb + (int64_t)h * D;
-    const int64_t kvbase = (int64_t)b * p.kv_sb + (int64_t)h * D;
-    const __bf16 *Qb = (const __bf16 *)p.q + qbase;
-    const char *Kb = uniform_ptr((const char *)((const __bf16 *)p.k + kvbase));
-    const char *Vb = uniform_ptr((const char *)((const __bf16 *)p.v + kvbase));
-    const bool vote = p.mask_out != nullptr;
-    const bool ranges = p.rg.any != 0;
-
-    // keep-vector: a clear bit marks the tile in mask_out.  Must-skip tiles are
-    // never visited and never marked, so their bits start set.
-    if (tid < 2 * W)
-        keep[tid / W][tid % W] = ranges ? p.rg.skip_bits[tid % W] : 0u;
-
-    // this lane's query and its Q^T B-operand fragments
-    const int qi = qt * BM + wq * 32 + lq;
-    const bool qvalid = qt < Tq && qi < Nq;
-    bf16x8 qf[D / 16];
-#pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (qvalid)
-            x = *(const u32x4 *)(Qb + (int64_t)qi * rs + ds * 16 + 8 * g);
-        qf[ds] = __builtin_bit_cast(bf16x8, x);
-    }
+    const int rs2_0 = p.H * D * 2;  // token stride (bytes)
 
     // Direct-to-LDS slots of the A-waves, which load every step (fixed for the
     // kernel): DMA instruction i of A-wave wq fills LDS chunks
@@ -284,38 +264,9 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
     // the tensors.  All of it is scalar arithmetic.
     const uint32_t m0_k = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)LDS_VOID(kbuf) + wq * 64 * 16);
     const uint32_t m0_v = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)LDS_VOID(vbuf) + wq * 64 * 16);
-    const uint32_t koff = (uint32_t)(kr0 * rs2 + kc0);
-    const uint32_t voff = (uint32_t)(vr0 * rs2 + vc0);
-    struct DmaPlan {
-        const char *kb, *vb;
-        int st;
-        int bytes;  // bytes of the step's rows that exist: min(Nk - key0, HK) rows
-    };
-    auto plan_step = [&](int key0, int st) __attribute__((always_inline)) {
-        DmaPlan d;
-        d.st = st;
-        d.kb = Kb + (int64_t)key0 * rs2;
-        d.vb = Vb + (int64_t)key0 * rs2;
-        d.bytes = min(Nk - key0, HK) * rs2;
-        return d;
-    };
-    auto issue_dma = [&](const DmaPlan &d, int i) __attribute__((always_inline)) {
-        // bytes of instruction i's RPI rows that exist; max(x, 0) as a sign
-        // mask keeps the clamp in scalar instructions
-        int x = d.bytes - i * G::RPI * rs2;
-        x &= ~(x >> 31);
-        const uint32_t bytes = (uint32_t)min(x, G::RPI * rs2);
-        const int64_t blk = (int64_t)i * G::RPI * rs2;
-        // LDS destinations: this wave's base, made opaque so that the compiler
-        // adds the stage/instruction offset here instead of keeping one
-        // precomputed scalar per (stage, instruction) live across the loop
-        uint32_t kb0 = m0_k, vb0 = m0_v;
-        asm volatile("" : "+s"(kb0), "+s"(vb0));
-        const uint32_t o = (uint32_t)(d.st * G::CH * 16 + i * 4 * 64 * 16);
-        dma16(buffer_rsrc(d.kb + blk, bytes), koff, kb0 + o);
-        dma16(buffer_rsrc(d.vb + blk, bytes), voff, vb0 + o);
-    };
-
+    uint32_t koff = (uint32_t)(kr0 * rs2_0 + kc0);
+    uint32_t voff = (uint32_t)(vr0 * rs2_0 + vc0);
+    asm volatile("" : "+v"(koff), "+v"(voff));
     // This lane's slot as a source of the transposed V read: key row 8g + a of
     // the 16-key group, 4 head-dim entries starting at sigma(16*(lane/16 % 2) + 4b),
     // where lane % 16 = 4a + b.  The lane that receives column i of a 32-entry
@@ -343,385 +294,480 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2)
         asm volatile("" : "+v"(kaddr[ds]));
     }
 
-    f32x16 O[D / 32];
-#pragma unroll
-    for (int eb = 0; eb < D / 32; ++eb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-            O[eb][v] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-    float m_before = -INFINITY, m_tile = -INFINITY;
-    f32x16 S[HK / 32];       // raw logits of the step between QK^T and softmax
-    bf16x8 P[HK / 16];       // weights of the step between softmax and PV
-#pragma unroll
-    for (int kb = 0; kb < HK / 32; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-            S[kb][v] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < HK / 16; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            P[ks][j] = (__bf16)0.f;
-
-    // ---- the union walk of the two q-tiles, built once into LDS ----
-    // Live tiles per mask word: from the Skip-Lists (LIST) or from mask_in with
-    // the token ranges applied (must-skip tiles out, must-do tiles in).  A
-    // q-tile that does not exist has none.
-    if (tid == 0)
-        nwalk = 0;  // no mask words (no keys): an empty walk
-    if (LIST) {
-        if (tid < 2 * W)
-            wlive[tid / W][tid % W] = 0u;
+    int own = (int)blockIdx.x;  // without counters: this workgroup's pair, then none
+    for (;;) {  // one q-tile pair per pass
+        // The parameters are read through a pointer the compiler cannot prove
+        // the same in every pass of this loop, so it loads them where they are
+        // used instead of holding some forty of them in scalar registers for the
+        // whole kernel (which spilled).  p is the first kernel argument: it sits
+        // at offset 0 of the argument segment.
+        typedef __attribute__((address_space(4))) const FwdParams cparams;
+        cparams *pp = (cparams *)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(pp));
+        cparams &prm = *pp;
+        // the next q-tile pair: a ticket, or this workgroup's own pair once
+        if (threadIdx.x == 0)
+            s_pair = prm.sched ? (int)atomicAdd(prm.sched, 1u) : own;
+        own = npairs;
         __syncthreads();
+        const int pair = __builtin_amdgcn_readfirstlane(s_pair);
+        if (pair >= npairs)
+            break;
+        const int Nq = prm.Nq, Nk = prm.Nk, H = prm.H, Tq = prm.Tq, Tk = prm.Tk, W = prm.W;
+        const int Tq2 = (Tq + 1) >> 1;
+        const int rs = H * D;                    // token stride (elements)
+        const int rs2 = rs * 2;                  // token stride (bytes)
+        const bool vote = prm.mask_out != nullptr;
+        const bool ranges = prm.rg.any != 0;
+
+        const int pq = (int)(pair % Tq2);
+        const int64_t bh = pair / Tq2;
+        const int h = (int)(bh % H), b = (int)(bh / H);
+        const bool has_b = 2 * pq + 1 < Tq;
+        const int64_t row_a = bh * Tq + 2 * pq;  // q-tile B is row_a + 1
+        const int qt = 2 * pq + half;            // this wave's q-tile
+        const int64_t qbase = (int64_t)b * prm.q_sb + (int64_t)h * D;
+        const int64_t kvbase = (int64_t)b * prm.kv_sb + (int64_t)h * D;
+        const __bf16 *Qb = (const __bf16 *)prm.q + qbase;
+        const char *Kb = uniform_ptr((const char *)((const __bf16 *)prm.k + kvbase));
+        const char *Vb = uniform_ptr((const char *)((const __bf16 *)prm.v + kvbase));
+
+        // keep-vector: a clear bit marks the tile in mask_out.  Must-skip tiles are
+        // never visited and never marked, so their bits start set.
+        if (tid < 2 * W)
+            keep[tid / W][tid % W] = ranges ? prm.rg.skip_bits[tid % W] : 0u;
+
+        // this lane's query and its Q^T B-operand fragments
+        const int qi = qt * BM + wq * 32 + lq;
+        const bool qvalid = qt < Tq && qi < Nq;
+        bf16x8 qf[D / 16];
 #pragma unroll
-        for (int hq = 0; hq < 2; ++hq) {
-            if (hq == 1 && !has_b)
-                break;
-            const int32_t *l = p.skiplist + (row_a + hq) * (1 + Tk);
-            const int c = min(max(l[0], 0), Tk);
-            for (int i = tid; i < c; i += NT) {
-                const int kt = l[1 + i];
-                if (kt >= 0 && kt < Tk)
-                    atomicOr(&wlive[hq][kt >> 5], 1u << (kt & 31));
-            }
+        for (int ds = 0; ds < D / 16; ++ds) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (qvalid)
+                x = *(const u32x4 *)(Qb + (int64_t)qi * rs + ds * 16 + 8 * g);
+            qf[ds] = __builtin_bit_cast(bf16x8, x);
         }
-    } else if (tid < 2 * W) {
-        const int hq = tid / W, w = tid % W;
-        uint32_t bits = 0u;
-        if (hq == 0 || has_b) {
-            bits = p.mask_in ? ~p.mask_in[(row_a + hq) * W + w] : 0xffffffffu;
-            if (ranges)
-                bits = (bits & ~p.rg.skip_bits[w]) | p.rg.do_bits[w];
-            if (w == W - 1 && (Tk & 31))
-                bits &= (1u << (Tk & 31)) - 1u;
-        }
-        wlive[hq][w] = bits;
-    }
-    __syncthreads();
-    if (tid < W)
-        wcnt[tid] = __builtin_popcount(wlive[0][tid] | wlive[1][tid]);
-    __syncthreads();
-    if (tid < W) {
-        // descending order: the tiles of the words above this one come first
-        int pos = 0;
-        for (int w = W - 1; w > tid; --w)
-            pos += wcnt[w];
-        const uint32_t a = wlive[0][tid], bb = wlive[1][tid];
-        uint32_t u = a | bb;
-        while (u) {
-            const int bit = 31 - __builtin_clz(u);
-            u &= ~(1u << bit);
-            walk[pos++] = (uint16_t)((tid * 32 + bit) | (((a >> bit) & 1u) << 12) | (((bb >> bit) & 1u) << 13));
-        }
+
+        struct DmaPlan {
+            const char *kb, *vb;
+            int st;
+            int bytes;  // bytes of the step's rows that exist: min(Nk - key0, HK) rows
+        };
+        auto plan_step = [&](int key0, int st) __attribute__((always_inline)) {
+            DmaPlan d;
+            d.st = st;
+            d.kb = Kb + (int64_t)key0 * rs2;
+            d.vb = Vb + (int64_t)key0 * rs2;
+            d.bytes = min(Nk - key0, HK) * rs2;
+            return d;
+        };
+        auto issue_dma = [&](const DmaPlan &d, int i) __attribute__((always_inline)) {
+            // bytes of instruction i's RPI rows that exist; max(x, 0) as a sign
+            // mask keeps the clamp in scalar instructions
+            int x = d.bytes - i * G::RPI * rs2;
+            x &= ~(x >> 31);
+            const uint32_t bytes = (uint32_t)min(x, G::RPI * rs2);
+            const int64_t blk = (int64_t)i * G::RPI * rs2;
+            // LDS destinations: this wave's base, made opaque so that the compiler
+            // adds the stage/instruction offset here instead of keeping one
+            // precomputed scalar per (stage, instruction) live across the loop
+            uint32_t kb0 = m0_k, vb0 = m0_v;
+            asm volatile("" : "+s"(kb0), "+s"(vb0));
+            const uint32_t o = (uint32_t)(d.st * G::CH * 16 + i * 4 * 64 * 16);
+            dma16(buffer_rsrc(d.kb + blk, bytes), koff, kb0 + o);
+            dma16(buffer_rsrc(d.vb + blk, bytes), voff, vb0 + o);
+        };
+
+        f32x16 O[D / 32];
+#pragma unroll
+        for (int eb = 0; eb < D / 32; ++eb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                O[eb][v] = 0.f;
+        float m_run = -INFINITY, l_run = 0.f;
+        float m_before = -INFINITY, m_tile = -INFINITY;
+        f32x16 S[HK / 32];       // raw logits of the step between QK^T and softmax
+        bf16x8 P[HK / 16];       // weights of the step between softmax and PV
+#pragma unroll
+        for (int kb = 0; kb < HK / 32; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                S[kb][v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < HK / 16; ++ks)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                P[ks][j] = (__bf16)0.f;
+
+        // ---- the union walk of the two q-tiles, built once into LDS ----
+        // Live tiles per mask word: from the Skip-Lists (LIST) or from mask_in with
+        // the token ranges applied (must-skip tiles out, must-do tiles in).  A
+        // q-tile that does not exist has none.
         if (tid == 0)
-            nwalk = pos;
-    }
-    __syncthreads();
-
-    // The walk is read 64 entries at a time, one per lane, and stepped with
-    // readlane: one scalar cursor, no per-tile memory round trip.
-    const int n_walk = __builtin_amdgcn_readfirstlane(nwalk);
-    int g_idx = 0, g_sub = 0, g_kt = -1, g_fl = 0;
-    uint32_t chunk = lane < n_walk ? walk[lane] : 0u;
-    if (n_walk > 0) {
-        const int e = __builtin_amdgcn_readfirstlane((int)chunk);
-        g_kt = e & 0xfff;
-        g_fl = e >> 12;
-    }
-    auto gen = [&]() __attribute__((always_inline)) {
-        // wave-uniform by construction; readfirstlane lets the compiler keep
-        // the step (and the load addresses built from it) in scalar registers
-        Step s;
-        s.kt = __builtin_amdgcn_readfirstlane(g_kt);
-        s.sub = __builtin_amdgcn_readfirstlane(g_sub);
-        s.fl = __builtin_amdgcn_readfirstlane(g_fl);
-        s.key0 = s.kt * BN + s.sub * HK;
-        if (g_kt >= 0 && ++g_sub == SPT) {
-            g_sub = 0;
-            if (++g_idx >= n_walk) {
-                g_kt = -1;
-            } else {
-                if ((g_idx & 63) == 0)
-                    chunk = g_idx + lane < n_walk ? walk[g_idx + lane] : 0u;
-                const int e = __builtin_amdgcn_readlane((int)chunk, g_idx & 63);
-                g_kt = e & 0xfff;
-                g_fl = e >> 12;
+            nwalk = 0;  // no mask words (no keys): an empty walk
+        if (LIST) {
+            if (tid < 2 * W)
+                wlive[tid / W][tid % W] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int hq = 0; hq < 2; ++hq) {
+                if (hq == 1 && !has_b)
+                    break;
+                const int32_t *l = prm.skiplist + (row_a + hq) * (1 + Tk);
+                const int c = min(max(l[0], 0), Tk);
+                for (int i = tid; i < c; i += NT) {
+                    const int kt = l[1 + i];
+                    if (kt >= 0 && kt < Tk)
+                        atomicOr(&wlive[hq][kt >> 5], 1u << (kt & 31));
+                }
             }
+        } else if (tid < 2 * W) {
+            const int hq = tid / W, w = tid % W;
+            uint32_t bits = 0u;
+            if (hq == 0 || has_b) {
+                bits = prm.mask_in ? ~prm.mask_in[(row_a + hq) * W + w] : 0xffffffffu;
+                if (ranges)
+                    bits = (bits & ~prm.rg.skip_bits[w]) | prm.rg.do_bits[w];
+                if (w == W - 1 && (Tk & 31))
+                    bits &= (1u << (Tk & 31)) - 1u;
+            }
+            wlive[hq][w] = bits;
         }
-        return s;
-    };
-    auto mine = [&](const Step &s) __attribute__((always_inline)) { return s.kt >= 0 && ((s.fl >> half) & 1); };
-    auto act = [&](const Step &s) __attribute__((always_inline)) { return mine(s) && s.key0 < Nk; };
-    auto loadable = [&](const Step &s) __attribute__((always_inline)) { return s.kt >= 0 && s.key0 < Nk; };
+        __syncthreads();
+        if (tid < W)
+            wcnt[tid] = __builtin_popcount(wlive[0][tid] | wlive[1][tid]);
+        __syncthreads();
+        if (tid < W) {
+            // descending order: the tiles of the words above this one come first
+            int pos = 0;
+            for (int w = W - 1; w > tid; --w)
+                pos += wcnt[w];
+            const uint32_t a = wlive[0][tid], bb = wlive[1][tid];
+            uint32_t u = a | bb;
+            while (u) {
+                const int bit = 31 - __builtin_clz(u);
+                u &= ~(1u << bit);
+                walk[pos++] = (uint16_t)((tid * 32 + bit) | (((a >> bit) & 1u) << 12) | (((bb >> bit) & 1u) << 13));
+            }
+            if (tid == 0)
+                nwalk = pos;
+        }
+        __syncthreads();
 
-    // ---- O^T += V^T P^T over one step (V in LDS stage vst) ----
-    // MFMA order ks-major over the D/32 independent accumulators; each
-    // transposed V read is issued AHEAD MFMAs before its use.
-    auto pv_gemm = [&](int vs) __attribute__((always_inline)) {
-        constexpr int NEB = D / 32, NM = NEB * (HK / 16);
-        // MFMA m = ks*NEB + eb; its operand is read AHEAD MFMAs earlier
-        s16x8 vf[NM];
-        auto rd = [&](int m) __attribute__((always_inline)) {
-            const int ks = m / NEB, eb = m % NEB;
-            typedef __attribute__((address_space(3))) char lchar;
-            lchar *va = (lchar *)(size_t)vaddr[eb] + vs * G::CH * 16 + 16 * ks * G::CPR * 16;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)va);
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(va + 4 * G::CPR * 16));
-            vf[m] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        // The walk is read 64 entries at a time, one per lane, and stepped with
+        // readlane: one scalar cursor, no per-tile memory round trip.
+        const int n_walk = __builtin_amdgcn_readfirstlane(nwalk);
+        int g_idx = 0, g_sub = 0, g_kt = -1, g_fl = 0;
+        uint32_t chunk = lane < n_walk ? walk[lane] : 0u;
+        if (n_walk > 0) {
+            const int e = __builtin_amdgcn_readfirstlane((int)chunk);
+            g_kt = e & 0xfff;
+            g_fl = e >> 12;
+        }
+        auto gen = [&]() __attribute__((always_inline)) {
+            // wave-uniform by construction; readfirstlane lets the compiler keep
+            // the step (and the load addresses built from it) in scalar registers
+            Step s;
+            s.kt = __builtin_amdgcn_readfirstlane(g_kt);
+            s.sub = __builtin_amdgcn_readfirstlane(g_sub);
+            s.fl = __builtin_amdgcn_readfirstlane(g_fl);
+            s.key0 = s.kt * BN + s.sub * HK;
+            if (g_kt >= 0 && ++g_sub == SPT) {
+                g_sub = 0;
+                if (++g_idx >= n_walk) {
+                    g_kt = -1;
+                } else {
+                    if ((g_idx & 63) == 0)
+                        chunk = g_idx + lane < n_walk ? walk[g_idx + lane] : 0u;
+                    const int e = __builtin_amdgcn_readlane((int)chunk, g_idx & 63);
+                    g_kt = e & 0xfff;
+                    g_fl = e >> 12;
+                }
+            }
+            return s;
         };
-#pragma unroll
-        for (int m = 0; m < AHEAD; ++m)
-            rd(m);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            if (m + AHEAD < NM)
-                rd(m + AHEAD);
-            O[m % NEB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[m]), P[m / NEB],
-                                                                 O[m % NEB], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * AHEAD, 0);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            if (m + AHEAD < NM)
-                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-        }
-    };
+        auto mine = [&](const Step &s) __attribute__((always_inline)) { return s.kt >= 0 && ((s.fl >> half) & 1); };
+        auto act = [&](const Step &s) __attribute__((always_inline)) { return mine(s) && s.key0 < Nk; };
+        auto loadable = [&](const Step &s) __attribute__((always_inline)) { return s.kt >= 0 && s.key0 < Nk; };
 
-    // ---- S^T = K Q^T over one step (K in LDS stage kst), raw logits ----
-    // MFMA order ds-major over the two 32-key blocks; one K read per MFMA,
-    // issued AHEAD MFMAs before its use.  With WD the loads of the next step
-    // (`dma`) go out one per two MFMAs.
-    auto s_gemm = [&](int ks_, const DmaPlan &dma, auto with_dma) __attribute__((always_inline)) {
-        constexpr bool WD = decltype(with_dma)::value;
-        constexpr int NDS = D / 16, NM = (HK / 32) * NDS;
-        static_assert(NM == 4 * G::IPA, "one load pair per four MFMAs");
-        // Row kb*32 + lq, chunk (2*ds + g) ^ k_swz(row) = 2*ds ^ kc: the swizzle
-        // depends on the row only through lq (kaddr).
-        // MFMA m = ds*2 + kb; its K fragment is read AHEAD MFMAs earlier.
-        // The first MFMA of each accumulator takes a zero C operand (an inline
-        // constant), so S needs no clearing moves.
-        u32x4 kf[NM];
-        auto rd = [&](int m) __attribute__((always_inline)) {
-            const int ds = m >> 1, kb = m & 1;
-            typedef __attribute__((address_space(3))) u32x4 lvec;
-            kf[m] = *(lvec *)((__attribute__((address_space(3))) char *)(size_t)kaddr[ds] +
-                              (ks_ * G::CH + kb * 32 * G::CPR) * 16);
+        // ---- O^T += V^T P^T over one step (V in LDS stage vst) ----
+        // MFMA order ks-major over the D/32 independent accumulators; each
+        // transposed V read is issued AHEAD MFMAs before its use.
+        auto pv_gemm = [&](int vs) __attribute__((always_inline)) {
+            constexpr int NEB = D / 32, NM = NEB * (HK / 16);
+            // MFMA m = ks*NEB + eb; its operand is read AHEAD MFMAs earlier
+            s16x8 vf[NM];
+            auto rd = [&](int m) __attribute__((always_inline)) {
+                const int ks = m / NEB, eb = m % NEB;
+                typedef __attribute__((address_space(3))) char lchar;
+                lchar *va = (lchar *)(size_t)vaddr[eb] + vs * G::CH * 16 + 16 * ks * G::CPR * 16;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)va);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4 *)(va + 4 * G::CPR * 16));
+                vf[m] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+#pragma unroll
+            for (int m = 0; m < AHEAD; ++m)
+                rd(m);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                if (m + AHEAD < NM)
+                    rd(m + AHEAD);
+                O[m % NEB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[m]), P[m / NEB],
+                                                                     O[m % NEB], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * AHEAD, 0);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                if (m + AHEAD < NM)
+                    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+            }
         };
-#pragma unroll
-        for (int m = 0; m < AHEAD; ++m)
-            rd(m);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            if (m + AHEAD < NM)
-                rd(m + AHEAD);
-            const f32x16 zero = {};
-            S[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[m]), qf[m >> 1],
-                                                               m < 2 ? zero : S[m & 1], 0, 0, 0);
-            // one (K, V) pair per four MFMAs: NM = 4 * IPA for both head dims
-            if (WD && (m & 3) == 3)
-                issue_dma(dma, m >> 2);
-        }
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, AHEAD, 0);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            if (m + AHEAD < NM)
-                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-            if (WD && (m & 1))
-                __builtin_amdgcn_sched_group_barrier(SG_VMEM, 1, 0);
-        }
-    };
 
-    // VALU part of this wave's q-tile: online softmax of step s (logits in S),
-    // weights into P, then the QK-Skip vote once the whole tile has been seen.
-    auto valu_part = [&](const Step &s) __attribute__((always_inline)) {
-        if (mine(s) && s.sub == 0) {
-            m_before = m_run;
-            m_tile = -INFINITY;
-        }
-        if (act(s)) {
-            // keys past the end of the sequence do not exist
-            if (s.key0 + HK > Nk) {
+        // ---- S^T = K Q^T over one step (K in LDS stage kst), raw logits ----
+        // MFMA order ds-major over the two 32-key blocks; one K read per MFMA,
+        // issued AHEAD MFMAs before its use.  With WD the loads of the next step
+        // (`dma`) go out one per two MFMAs.
+        auto s_gemm = [&](int ks_, const DmaPlan &dma, auto with_dma) __attribute__((always_inline)) {
+            constexpr bool WD = decltype(with_dma)::value;
+            constexpr int NDS = D / 16, NM = (HK / 32) * NDS;
+            static_assert(NM == 4 * G::IPA, "one load pair per four MFMAs");
+            // Row kb*32 + lq, chunk (2*ds + g) ^ k_swz(row) = 2*ds ^ kc: the swizzle
+            // depends on the row only through lq (kaddr).
+            // MFMA m = ds*2 + kb; its K fragment is read AHEAD MFMAs earlier.
+            // The first MFMA of each accumulator takes a zero C operand (an inline
+            // constant), so S needs no clearing moves.
+            u32x4 kf[NM];
+            auto rd = [&](int m) __attribute__((always_inline)) {
+                const int ds = m >> 1, kb = m & 1;
+                typedef __attribute__((address_space(3))) u32x4 lvec;
+                kf[m] = *(lvec *)((__attribute__((address_space(3))) char *)(size_t)kaddr[ds] +
+                                  (ks_ * G::CH + kb * 32 * G::CPR) * 16);
+            };
+#pragma unroll
+            for (int m = 0; m < AHEAD; ++m)
+                rd(m);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                if (m + AHEAD < NM)
+                    rd(m + AHEAD);
+                const f32x16 zero = {};
+                S[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[m]), qf[m >> 1],
+                                                                   m < 2 ? zero : S[m & 1], 0, 0, 0);
+                // one (K, V) pair per four MFMAs: NM = 4 * IPA for both head dims
+                if (WD && (m & 3) == 3)
+                    issue_dma(dma, m >> 2);
+            }
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, AHEAD, 0);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                if (m + AHEAD < NM)
+                    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+                if (WD && (m & 1))
+                    __builtin_amdgcn_sched_group_barrier(SG_VMEM, 1, 0);
+            }
+        };
+
+        // VALU part of this wave's q-tile: online softmax of step s (logits in S),
+        // weights into P, then the QK-Skip vote once the whole tile has been seen.
+        auto valu_part = [&](const Step &s) __attribute__((always_inline)) {
+            if (mine(s) && s.sub == 0) {
+                m_before = m_run;
+                m_tile = -INFINITY;
+            }
+            if (act(s)) {
+                // keys past the end of the sequence do not exist
+                if (s.key0 + HK > Nk) {
+#pragma unroll
+                    for (int kb = 0; kb < HK / 32; ++kb)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            if (s.key0 + kb * 32 + 16 * (v >> 3) + 8 * g + (v & 7) >= Nk)
+                                S[kb][v] = -INFINITY;
+                }
+                // step-local max (log2 units)
+                float mx = -INFINITY;
 #pragma unroll
                 for (int kb = 0; kb < HK / 32; ++kb)
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
-                        if (s.key0 + kb * 32 + 16 * (v >> 3) + 8 * g + (v & 7) >= Nk)
-                            S[kb][v] = -INFINITY;
-            }
-            // step-local max (log2 units)
-            float mx = -INFINITY;
+                        mx = fmaxf(mx, S[kb][v]);
+                mx = fmaxf(mx, other_half(mx));
+                const float m_loc = mx * c2;
+                m_tile = fmaxf(m_tile, m_loc);
+                // Exponents are taken against the exact running max, so the largest
+                // weight of a row is exactly 1 (exact in bf16); O and l are rescaled
+                // only when some query's max moved (wave-uniform test).
+                const float m_new = fmaxf(m_run, m_loc);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                const float neg = -m_new;
+                float rsum = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < HK / 32; ++kb)
+                for (int kb = 0; kb < HK / 32; ++kb)
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    mx = fmaxf(mx, S[kb][v]);
-            mx = fmaxf(mx, other_half(mx));
-            const float m_loc = mx * c2;
-            m_tile = fmaxf(m_tile, m_loc);
-            // Exponents are taken against the exact running max, so the largest
-            // weight of a row is exactly 1 (exact in bf16); O and l are rescaled
-            // only when some query's max moved (wave-uniform test).
-            const float m_new = fmaxf(m_run, m_loc);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            const float neg = -m_new;
-            float rsum = 0.f;
+                    for (int v = 0; v < 16; ++v) {
+                        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][v], c2, neg));
+                        rsum += pv;
+                        P[kb * 2 + (v >> 3)][v & 7] = (__bf16)pv;
+                    }
+                l_run = l_run * alpha + rsum;
+                m_run = m_new;
+                if (__ballot(alpha != 1.0f) != 0ull) {
 #pragma unroll
-            for (int kb = 0; kb < HK / 32; ++kb)
+                    for (int eb = 0; eb < D / 32; ++eb)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][v], c2, neg));
-                    rsum += pv;
-                    P[kb * 2 + (v >> 3)][v & 7] = (__bf16)pv;
+                        for (int v = 0; v < 16; ++v)
+                            O[eb][v] *= alpha;
                 }
-            l_run = l_run * alpha + rsum;
-            m_run = m_new;
-            if (__ballot(alpha != 1.0f) != 0ull) {
-#pragma unroll
-                for (int eb = 0; eb < D / 32; ++eb)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        O[eb][v] *= alpha;
             }
-        }
-        if (vote && mine(s) && s.sub == SPT - 1) {
-            // a must-do tile is never marked
-            const bool must_do = ranges && ((p.rg.do_bits[s.kt >> 5] >> (s.kt & 31)) & 1u);
-            const bool keep_lane = must_do || (qvalid && !(m_tile - m_before < tau2));
-            if (__ballot(keep_lane) != 0ull && lane == 0)
-                lds_or(&keep[half][s.kt >> 5], 1u << (s.kt & 31));
-        }
-    };
-
-    // Every A-wave issues exactly 2*IPA loads per step (real, or empty-range
-    // loads that write zeros to a stage nobody reads and touch no memory), so
-    // that "all but the last 2*IPA loads done" means "the step before the last
-    // one has landed".
-    constexpr int VM_KEEP = 2 * G::IPA;
-    constexpr int WAIT_KEEP = (VM_KEEP & 15) | (7 << 4) | (15 << 8) | ((VM_KEEP >> 4) << 14);  // vmcnt only
-    constexpr int WAIT_ALL = (7 << 4) | (15 << 8);  // vmcnt(0) only
-    auto load_step = [&](const Step &s, int dst) __attribute__((always_inline)) {
-        if (Nk <= 0)
-            return;  // no key rows at all
-        const DmaPlan d = plan_step(loadable(s) ? s.key0 : Nk, dst);
-#pragma unroll
-        for (int i = 0; i < G::IPA; ++i)
-            issue_dma(d, i);
-    };
-
-    Step sp = {-1, 0, 0, 0};  // step u - 1
-    Step sc = gen();          // step u
-    Step sn = gen();          // step u + 1
-    Step sn2 = gen();         // step u + 2
-    if (half == 0) {
-        load_step(sc, 0);
-        load_step(sn, 1);
-        __builtin_amdgcn_s_waitcnt(WAIT_KEEP);  // step 0 has landed
-    }
-    __syncthreads();
-
-    // Step u, with its K in stage ST = u mod 4, step u - 1's V in stage
-    // (ST + 3) mod 4, step u + 1 in flight to stage (ST + 1) mod 4 and step
-    // u + 2 loading into stage (ST + 2) mod 4.  Each half runs its own copy of
-    // the loop, with its two parts in its own order, so that neither path
-    // carries the other's registers; both pass the same barrier once per step.
-    // Returns false once both the step and the one before it are past the end.
-    auto run = [&](auto half_tag) __attribute__((always_inline)) {
-        constexpr int HF = decltype(half_tag)::value;
-        // MFMA part: PV of step u - 1, then QK^T of step u; the A-waves load
-        // step u + 2 meanwhile (spread over the QK^T MFMAs).
-        auto mfma_part = [&](int vst, int kst, int lst) __attribute__((always_inline)) {
-            if (act(sp))
-                pv_gemm(vst);
-            if (HF == 0) {
-                if (act(sc)) {
-                    s_gemm(kst, plan_step(loadable(sn2) ? sn2.key0 : Nk, lst), std::true_type{});
-                } else {
-                    load_step(sn2, lst);
-                }
-            } else if (act(sc)) {
-                s_gemm(kst, plan_step(0, lst), std::false_type{});
+            if (vote && mine(s) && s.sub == SPT - 1) {
+                // a must-do tile is never marked
+                const bool must_do = ranges && ((prm.rg.do_bits[s.kt >> 5] >> (s.kt & 31)) & 1u);
+                const bool keep_lane = must_do || (qvalid && !(m_tile - m_before < tau2));
+                if (__ballot(keep_lane) != 0ull && lane == 0)
+                    lds_or(&keep[half][s.kt >> 5], 1u << (s.kt & 31));
             }
         };
-        auto iter = [&](auto stage_tag) __attribute__((always_inline)) -> bool {
-            constexpr int ST = decltype(stage_tag)::value;
-            if (sc.kt < 0 && sp.kt < 0)
-                return false;
-            constexpr int kst = ST, lst = (ST + 2) & 3, vst = (ST + 3) & 3;
-            // A: MFMAs, then softmax; B: softmax, then MFMAs.  No barrier in
-            // between: the opposite orders alone keep one wave of each SIMD on
-            // the matrix core while the other is on the vector ALU.
-            if (HF == 0)
-                mfma_part(vst, kst, lst);
-            else
-                valu_part(sp);
-            if (HF == 0)
-                valu_part(sc);
-            else
-                mfma_part(vst, kst, lst);
-            // step u + 1 has landed (step u + 2 may still be in flight)
-            __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            sp = sc;
-            sc = sn;
-            sn = sn2;
-            sn2 = gen();
-            return true;
-        };
-        for (;;) {
-            if (!iter(std::integral_constant<int, 0>{}))
-                break;
-            if (!iter(std::integral_constant<int, 1>{}))
-                break;
-            if (!iter(std::integral_constant<int, 2>{}))
-                break;
-            if (!iter(std::integral_constant<int, 3>{}))
-                break;
-        }
-    };
-    if (half == 0)
-        run(std::integral_constant<int, 0>{});
-    else
-        run(std::integral_constant<int, 1>{});
-    __builtin_amdgcn_s_waitcnt(WAIT_ALL);
-    __syncthreads();  // every load landed before the workgroup's LDS is released
 
-    // ---- epilogue ----
-    const float l_tot = l_run + other_half(l_run);
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    if (qvalid) {
-        __bf16 *Ob = (__bf16 *)p.out + (int64_t)b * p.o_sb + (int64_t)h * D + (int64_t)qi * rs;
+        // Every A-wave issues exactly 2*IPA loads per step (real, or empty-range
+        // loads that write zeros to a stage nobody reads and touch no memory), so
+        // that "all but the last 2*IPA loads done" means "the step before the last
+        // one has landed".
+        constexpr int VM_KEEP = 2 * G::IPA;
+        constexpr int WAIT_KEEP = (VM_KEEP & 15) | (7 << 4) | (15 << 8) | ((VM_KEEP >> 4) << 14);  // vmcnt only
+        constexpr int WAIT_ALL = (7 << 4) | (15 << 8);  // vmcnt(0) only
+        auto load_step = [&](const Step &s, int dst) __attribute__((always_inline)) {
+            if (Nk <= 0)
+                return;  // no key rows at all
+            const DmaPlan d = plan_step(loadable(s) ? s.key0 : Nk, dst);
 #pragma unroll
-        for (int eb = 0; eb < D / 32; ++eb) {
-            bf16x8 lo, hi;
-#pragma unroll
-            for (int v = 0; v < 8; ++v) {
-                lo[v] = (__bf16)(O[eb][v] * inv);
-                hi[v] = (__bf16)(O[eb][v + 8] * inv);
-            }
-            u32x4 *dst = (u32x4 *)(Ob + eb * 32 + 16 * g);
-            dst[0] = __builtin_bit_cast(u32x4, lo);
-            dst[1] = __builtin_bit_cast(u32x4, hi);
+            for (int i = 0; i < G::IPA; ++i)
+                issue_dma(d, i);
+        };
+
+        Step sp = {-1, 0, 0, 0};  // step u - 1
+        Step sc = gen();          // step u
+        Step sn = gen();          // step u + 1
+        Step sn2 = gen();         // step u + 2
+        if (half == 0) {
+            load_step(sc, 0);
+            load_step(sn, 1);
+            __builtin_amdgcn_s_waitcnt(WAIT_KEEP);  // step 0 has landed
         }
-        if (p.lse && g == 0)
-            p.lse[bh * Nq + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-    }
-    if (vote) {
         __syncthreads();
-        if (tid < 2 * W) {
-            const int hh = tid / W, w = tid % W;
-            if (hh == 0 || has_b) {
-                const int64_t r = row_a + hh;
-                uint32_t valid = 0xffffffffu;
-                if (w == W - 1 && (Tk & 31))
-                    valid = (1u << (Tk & 31)) - 1u;
-                const uint32_t in = p.mask_in ? p.mask_in[r * W + w] : 0u;
-                p.mask_out[r * W + w] = (in | ~keep[hh][w]) & valid;
+
+        // Step u, with its K in stage ST = u mod 4, step u - 1's V in stage
+        // (ST + 3) mod 4, step u + 1 in flight to stage (ST + 1) mod 4 and step
+        // u + 2 loading into stage (ST + 2) mod 4.  Each half runs its own copy of
+        // the loop, with its two parts in its own order, so that neither path
+        // carries the other's registers; both pass the same barrier once per step.
+        // Returns false once both the step and the one before it are past the end.
+        auto run = [&](auto half_tag) __attribute__((always_inline)) {
+            constexpr int HF = decltype(half_tag)::value;
+            // MFMA part: PV of step u - 1, then QK^T of step u; the A-waves load
+            // step u + 2 meanwhile (spread over the QK^T MFMAs).
+            auto mfma_part = [&](int vst, int kst, int lst) __attribute__((always_inline)) {
+                if (act(sp))
+                    pv_gemm(vst);
+                if (HF == 0) {
+                    if (act(sc)) {
+                        s_gemm(kst, plan_step(loadable(sn2) ? sn2.key0 : Nk, lst), std::true_type{});
+                    } else {
+                        load_step(sn2, lst);
+                    }
+                } else if (act(sc)) {
+                    s_gemm(kst, plan_step(0, lst), std::false_type{});
+                }
+            };
+            auto iter = [&](auto stage_tag) __attribute__((always_inline)) -> bool {
+                constexpr int ST = decltype(stage_tag)::value;
+                if (sc.kt < 0 && sp.kt < 0)
+                    return false;
+                constexpr int kst = ST, lst = (ST + 2) & 3, vst = (ST + 3) & 3;
+                // A: MFMAs, then softmax; B: softmax, then MFMAs.  No barrier in
+                // between: the opposite orders alone keep one wave of each SIMD on
+                // the matrix core while the other is on the vector ALU.
+                if (HF == 0)
+                    mfma_part(vst, kst, lst);
+                else
+                    valu_part(sp);
+                if (HF == 0)
+                    valu_part(sc);
+                else
+                    mfma_part(vst, kst, lst);
+                // step u + 1 has landed (step u + 2 may still be in flight)
+                __builtin_amdgcn_s_waitcnt(WAIT_KEEP);
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                sp = sc;
+                sc = sn;
+                sn = sn2;
+                sn2 = gen();
+                return true;
+            };
+            for (;;) {
+                if (!iter(std::integral_constant<int, 0>{}))
+                    break;
+                if (!iter(std::integral_constant<int, 1>{}))
+                    break;
+                if (!iter(std::integral_constant<int, 2>{}))
+                    break;
+                if (!iter(std::integral_constant<int, 3>{}))
+                    break;
             }
+        };
+        if (half == 0)
+            run(std::integral_constant<int, 0>{});
+        else
+            run(std::integral_constant<int, 1>{});
+        __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+        __syncthreads();  // every load landed before the workgroup's LDS is released
+
+        // ---- epilogue ----
+        const float l_tot = l_run + other_half(l_run);
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        if (qvalid) {
+            __bf16 *Ob = (__bf16 *)prm.out + (int64_t)b * prm.o_sb + (int64_t)h * D + (int64_t)qi * rs;
+#pragma unroll
+            for (int eb = 0; eb < D / 32; ++eb) {
+                bf16x8 lo, hi;
+#pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    lo[v] = (__bf16)(O[eb][v] * inv);
+                    hi[v] = (__bf16)(O[eb][v + 8] * inv);
+                }
+                u32x4 *dst = (u32x4 *)(Ob + eb * 32 + 16 * g);
+                dst[0] = __builtin_bit_cast(u32x4, lo);
+                dst[1] = __builtin_bit_cast(u32x4, hi);
+            }
+            if (prm.lse && g == 0)
+                prm.lse[bh * Nq + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+        }
+        if (vote) {
+            __syncthreads();
+            if (tid < 2 * W) {
+                const int hh = tid / W, w = tid % W;
+                if (hh == 0 || has_b) {
+                    const int64_t r = row_a + hh;
+                    uint32_t valid = 0xffffffffu;
+                    if (w == W - 1 && (Tk & 31))
+                        valid = (1u << (Tk & 31)) - 1u;
+                    const uint32_t in = prm.mask_in ? prm.mask_in[r * W + w] : 0u;
+                    prm.mask_out[r * W + w] = (in | ~keep[hh][w]) & valid;
+                }
+            }
+        }
+    }  // pairs
+    // Every workgroup has drawn its last ticket before it counts itself out
+    // here, so the last one out may clear both counters for the next launch.
+    if (p.sched && threadIdx.x == 0) {
+        __threadfence();
+        if (atomicAdd(p.sched + 1, 1u) == gridDim.x - 1) {
+            atomicExch(p.sched, 0u);
+            atomicExch(p.sched + 1, 0u);
         }
     }
 }
@@ -732,12 +778,27 @@ hipError_t launch(const FwdParams &p, hipStream_t stream)
     const double LOG2E = 1.4426950408889634;
     const float c2 = (float)(p.scale * LOG2E);
     const float tau2 = isinf(p.tau) ? (float)p.tau : (float)(p.tau * LOG2E);
-    const int64_t groups = (int64_t)p.B * p.H * ((p.Tq + 1) / 2);
+    const int64_t pairs = (int64_t)p.B * p.H * ((p.Tq + 1) / 2);
+    if (pairs == 0)
+        return hipSuccess;
+    // with counters: one workgroup per compute unit (the LDS holds one), at
+    // most one per pair
+    int64_t grid = pairs;
+    if (p.sched) {
+        int dev = 0, ncu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess)
+            e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess)
+            return e;
+        grid = std::min<int64_t>(pairs, std::max(ncu, 1));
+    }
     if (p.skiplist)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, true>), dim3((unsigned)groups), dim3(NT), 0, stream, p, c2, tau2);
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, true>), dim3((unsigned)grid), dim3(NT), 0, stream, p, c2, tau2,
+                           (int)pairs);
     else
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, false>), dim3((unsigned)groups), dim3(NT), 0, stream, p, c2,
-                           tau2);
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, false>), dim3((unsigned)grid), dim3(NT), 0, stream, p, c2, tau2,
+                           (int)pairs);
     return hipGetLastError();
 }
 

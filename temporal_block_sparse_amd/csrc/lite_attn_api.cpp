@@ -212,7 +212,8 @@ const char *lite_attn_strerror(int code)
 
 int lite_attn_fwd(const lite_attn_desc *desc, const void *q, const void *k, const void *v,
                   const uint32_t *mask_in, uint32_t *mask_out, const int32_t *skiplist, float tau,
-                  float softmax_scale, void *out, float *lse, const lite_attn_ranges *ranges, void *stream)
+                  float softmax_scale, void *out, float *lse, const lite_attn_ranges *ranges, uint32_t *sched,
+                  void *stream)
 {
     Dims r;
     int rc = check_desc(desc, &r);
@@ -235,7 +236,8 @@ int lite_attn_fwd(const lite_attn_desc *desc, const void *q, const void *k, cons
     if (!q || !out || (desc->seqlen_kv > 0 && (!k || !v)))
         return LITE_ERR_NULL_ARG;  // k and v may be NULL when there are no keys
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(mask_in, 4) ||
-        !aligned(mask_out, 4) || !aligned(skiplist, 4) || !aligned(lse, 4) || !strides_aligned(desc, r))
+        !aligned(mask_out, 4) || !aligned(skiplist, 4) || !aligned(lse, 4) || !aligned(sched, 4) ||
+        !strides_aligned(desc, r))
         return LITE_ERR_MISALIGNED;
 
     const size_t esz = elem_size(desc->dtype);
@@ -258,6 +260,13 @@ int lite_attn_fwd(const lite_attn_desc *desc, const void *q, const void *k, cons
         return LITE_ERR_ALIAS;
     if (mask_out != mask_in && overlap(mask_out, mbytes, mask_in, mbytes))
         return LITE_ERR_ALIAS;
+    // the schedule counters are written by the kernel: they share no byte with any other buffer
+    const size_t cbytes = LITE_ATTN_SCHED_WORDS * sizeof(uint32_t);
+    const void *bufs[] = {q, k, v, out, lse, mask_in, mask_out, skiplist};
+    const size_t bufb[] = {qbytes, kvbytes, kvbytes, obytes, lbytes, mbytes, mbytes, sbytes};
+    for (int i = 0; i < 8; ++i)
+        if (overlap(sched, cbytes, bufs[i], bufb[i]))
+            return LITE_ERR_ALIAS;
 
     p.q = q;
     p.k = k;
@@ -283,14 +292,15 @@ int lite_attn_fwd(const lite_attn_desc *desc, const void *q, const void *k, cons
     p.rows = r.rows;
     p.tau = (double)tau;
     p.scale = (double)softmax_scale;
+    p.sched = desc->dtype == LITE_BF16 ? sched : nullptr;
 
     if (env_flag("LITE_ATTENTION_VERBOSE"))
         std::fprintf(stderr,
                      "[lite_attn] fwd %s d=%d tile=%dx%d B=%d Nq=%d Nk=%d H=%d rows=%lld Tk=%d mask_in=%d "
-                     "mask_out=%d skiplist=%d ranges=%d tau=%g\n",
+                     "mask_out=%d skiplist=%d ranges=%d sched=%d tau=%g\n",
                      desc->dtype == LITE_BF16 ? "bf16" : "fp32", p.D, p.BM, p.BN, p.B, p.Nq, p.Nk, p.H,
                      (long long)p.rows, p.Tk, mask_in != nullptr, mask_out != nullptr, skiplist != nullptr,
-                     p.rg.any, (double)tau);
+                     p.rg.any, p.sched != nullptr, (double)tau);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e =

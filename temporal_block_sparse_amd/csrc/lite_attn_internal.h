@@ -33,6 +33,7 @@ struct FwdParams {
     double tau;                // natural-log units; -inf = never mark
     double scale;              // softmax scale (> 0)
     TileRanges rg;
+    uint32_t *sched;           // bf16 path: 2 schedule counters (zero at rest), or null: one workgroup per pair
 };
 
 struct MergeParams {

@@ -23,6 +23,7 @@ LIB_PATH = os.environ.get("LITE_ATTN_LIBRARY") or os.path.join(_HERE, "liblite_a
 
 LITE_BF16, LITE_FP32 = 0, 1
 LITE_OK = 0
+SCHED_WORDS = 2  # LITE_ATTN_SCHED_WORDS
 MAX_MERGE_PARTS = 8
 ERRORS = {1: "LITE_ERR_NULL_ARG", 2: "LITE_ERR_BAD_SHAPE", 3: "LITE_ERR_UNSUPPORTED", 4: "LITE_ERR_BAD_THRESHOLD",
           5: "LITE_ERR_BAD_SCALE", 6: "LITE_ERR_MISALIGNED", 7: "LITE_ERR_ALIAS", 8: "LITE_ERR_HIP",
@@ -59,7 +60,7 @@ def _load():
     D = ctypes.POINTER(Desc)
     R = ctypes.POINTER(Ranges)
     lib.lite_attn_fwd.restype = ctypes.c_int
-    lib.lite_attn_fwd.argtypes = [D, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float, P, P, R, P]
+    lib.lite_attn_fwd.argtypes = [D, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float, P, P, R, P, P]
     lib.lite_attn_build_skiplist.restype = ctypes.c_int
     lib.lite_attn_build_skiplist.argtypes = [D, P, P, R, P]
     lib.lite_attn_reset_mask.restype = ctypes.c_int
@@ -186,6 +187,27 @@ def _ranges(must_do, must_skip):
     return r
 
 
+# Schedule counters of the forward, one buffer per (device, stream): calls on
+# one stream never overlap, so they may share it; the kernels leave it zero.
+_SCHED = {}
+
+
+def _sched_auto(stream_handle, device):
+    """The counters for calls on this stream, or None (one workgroup per pair)
+    while the current stream is being captured into a graph: a graph replayed
+    on another stream could then run at the same time as eager calls sharing
+    the buffer."""
+    key = (device.index, stream_handle.value or 0)
+    buf = _SCHED.get(key)
+    if buf is None:
+        if torch.cuda.is_current_stream_capturing():
+            return None
+        buf = torch.zeros(SCHED_WORDS, dtype=torch.int32, device=device)
+        torch.cuda.synchronize(device)  # zero before any stream uses it
+        _SCHED[key] = buf
+    return buf
+
+
 def desc_of(q, tile_m, tile_n, k=None, out=None):
     """Descriptor of the q (and k, v, out) tensors as passed to lite_attn_fwd."""
     B, N, H, D, qs, _ = _bshd(q)
@@ -199,13 +221,17 @@ def desc_of(q, tile_m, tile_n, k=None, out=None):
 
 
 def lite_attn_fwd(q, k, v, out, *, tile_m, tile_n, tau, softmax_scale=None, mask_in=None, mask_out=None,
-                  skiplist=None, lse=None, must_do=None, must_skip=None, stream=None):
+                  skiplist=None, lse=None, must_do=None, must_skip=None, sched="auto", stream=None):
     """C lite_attn_fwd on BSHD tensors: q and out [B, Nq, H, d], k and v
     [B, Nk, H, d], each a whole tensor or a sequence slice of one.
     mask_in/mask_out: int32 tensors of lite_attn_mask_words() words; skiplist:
     int32 of lite_attn_skiplist_len(); lse: fp32 [B, H, Nq]; must_do/must_skip:
-    the README's [start_0, end_0, ...] key ranges.  Raises LiteAttnError on a
-    non-zero return code."""
+    the README's [start_0, end_0, ...] key ranges.  sched: the schedule
+    counters (int32 tensor of SCHED_WORDS zeros), "auto" for the stream's own
+    (none while a graph is being captured), or None for one workgroup per
+    q-tile pair.  Raises LiteAttnError on a non-zero return code."""
+    if isinstance(sched, str) and sched != "auto":
+        raise ValueError('sched must be a tensor, "auto" or None')
     desc = desc_of(q, tile_m, tile_n, k, out)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(q.shape[-1])
@@ -217,12 +243,16 @@ def lite_attn_fwd(q, k, v, out, *, tile_m, tile_n, tau, softmax_scale=None, mask
         raise ValueError("v must be laid out like k")
     rg = _ranges(must_do, must_skip)
     mb = 4 * lite_attn_mask_words(desc)
+    st = _stream(stream)
+    if isinstance(sched, str):
+        sched = _sched_auto(st, q.device) if q.dtype == torch.bfloat16 and q.is_cuda else None
     _check(LIB.lite_attn_fwd(ctypes.byref(desc), _bshd(q)[5], _bshd(k)[5], _bshd(v)[5],
                              _buf(mask_in, mb, "mask_in"), _buf(mask_out, mb, "mask_out"),
                              _buf(skiplist, 4 * lite_attn_skiplist_len(desc), "skiplist"), float(tau),
                              float(softmax_scale), _bshd(out)[5],
                              _buf(lse, 4 * desc.batch * desc.heads * desc.seqlen, "lse", torch.float32),
-                             ctypes.byref(rg) if rg is not None else None, _stream(stream)))
+                             ctypes.byref(rg) if rg is not None else None,
+                             _buf(sched, 4 * SCHED_WORDS, "sched", torch.int32), st))
     return out
 
 

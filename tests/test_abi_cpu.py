@@ -34,11 +34,11 @@ def desc(**kw):
 
 
 def fwd(d, q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), mask_in=None, mask_out=None, skiplist=None,
-        tau=-3.0, scale=0.125, out=FAKE + (3 << 30), lse=None, ranges=None):
+        tau=-3.0, scale=0.125, out=FAKE + (3 << 30), lse=None, ranges=None, sched=None):
     P = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
     return la.LIB.lite_attn_fwd(ctypes.byref(d) if d is not None else None, P(q), P(k), P(v), P(mask_in),
                                 P(mask_out), P(skiplist), tau, scale, P(out), P(lse),
-                                ctypes.byref(ranges) if ranges is not None else None, None)
+                                ctypes.byref(ranges) if ranges is not None else None, P(sched), None)
 
 
 def merge(d, outs, lses, out, lse=None):
@@ -55,7 +55,7 @@ def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(la.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert la.LIB.lite_attn_abi_version() == 2
+    assert la.LIB.lite_attn_abi_version() == 3
 
 
 def test_sizes():
@@ -125,6 +125,32 @@ def test_aliasing():
     assert fwd(desc(), mask_in=m, mask_out=m + 4, q=None) == 1          # partial overlap is checked after NULL
     assert fwd(desc(), mask_in=m, mask_out=m + 4) == 7
     assert fwd(desc(), mask_in=m, mask_out=m, skiplist=m + 32) == 7      # mask_out overlaps the skip-list
+
+
+def test_schedule_counters_validation():
+    """The forward's schedule counters (LITE_ATTN_SCHED_WORDS words) are
+    written by the kernel: 4-byte aligned, and sharing no byte with any other
+    buffer of the call."""
+    c = FAKE + (7 << 30)
+    assert fwd(desc(), sched=c + 2) == 6
+    m = FAKE + (5 << 30)
+    assert fwd(desc(), sched=FAKE + 64) == 7                                  # inside q
+    assert fwd(desc(), sched=FAKE + (2 << 30)) == 7                           # at v
+    assert fwd(desc(), sched=FAKE + (3 << 30) + 4096) == 7                    # inside out
+    assert fwd(desc(), mask_in=m, mask_out=m, sched=m + 8) == 7              # inside the masks
+    assert fwd(desc(), lse=FAKE + (6 << 30), sched=FAKE + (6 << 30) - 4) == 7  # its last word is lse's first
+    # checked only when there is work: an empty call ignores it
+    assert fwd(desc(seqlen=0), q=None, k=None, v=None, out=None, sched=c + 2) == 0
+
+
+def test_binding_schedule_argument():
+    with pytest.raises(ValueError, match="sched must be"):
+        t = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
+        la.lite_attn_fwd(t, t.clone(), t.clone(), t.clone(), tile_m=128, tile_n=64, tau=-3.0, sched="tickets")
+    with pytest.raises(ValueError, match="sched holds"):
+        la._buf(torch.zeros(1, dtype=torch.int32), 4 * la.SCHED_WORDS, "sched", torch.int32)
+    with pytest.raises(ValueError, match="sched must be torch.int32"):
+        la._buf(torch.zeros(2, dtype=torch.int64), 4 * la.SCHED_WORDS, "sched", torch.int32)
 
 
 def test_empty_descriptor_is_a_noop():
