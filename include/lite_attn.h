@@ -191,6 +191,27 @@ int lite_attn_fwd(const lite_attn_desc *desc, const void *q, const void *k, cons
                   uint32_t *sched, void *stream);
 
 /*
+ * lite_attn_fwd_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): lite_attn_fwd with its schedule counters taken from the
+ * library instead of from a sched argument.  Same arguments otherwise, same
+ * validation, same results bit for bit.
+ * The counters are a static array of LITE_ATTN_SCHED_WORDS words per GPU,
+ * held until the process ends; its address on a device is looked up once, at
+ * the first call on that device.  Each call clears the counters with a fill
+ * kernel (no memset) and then runs the ticket schedule; nothing is allocated.
+ * The array's size does not grow with the call: every size lite_attn_fwd
+ * accepts fits, so no size is refused for lack of room.
+ * Every call on one GPU shares the array and finds the last call's contents:
+ * calls that overlap in time on one GPU (different streams, or graphs
+ * replayed concurrently) race on it and must not be made.
+ */
+int lite_attn_fwd_noalloc(const lite_attn_desc *desc, const void *q, const void *k, const void *v,
+                          const uint32_t *mask_in, uint32_t *mask_out, const int32_t *skiplist, float tau,
+                          float softmax_scale, void *out, float *lse, const lite_attn_ranges *ranges,
+                          void *stream);
+
+/*
  * lite_attn_build_skiplist -- compact each row of a Skip-Mask into its
  * Skip-List ([SKILL] "Skip-List for high sparsity"): the tiles the forward
  * would visit under this mask and these ranges, in visiting order.

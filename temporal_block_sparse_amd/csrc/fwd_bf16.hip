@@ -86,6 +86,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 namespace lite_attn {
@@ -803,6 +804,35 @@ hipError_t launch(const FwdParams &p, hipStream_t stream)
 }
 
 }  // namespace
+
+// Schedule counters for callers that cannot allocate (lite_attn_fwd_noalloc):
+// one static array per GPU, held until the process ends.  Host code never
+// uses its name as an address: each device's address comes from
+// hipGetSymbolAddress, called once per device with that device current.
+static __device__ __align__(256) uint32_t scratch[NOALLOC_SCHED_WORDS];
+
+hipError_t noalloc_sched(uint32_t **ptr)
+{
+    constexpr int MAX_DEVICES = 64;
+    static std::once_flag once[MAX_DEVICES];
+    static uint32_t *addr[MAX_DEVICES];
+    static hipError_t err[MAX_DEVICES];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= MAX_DEVICES)
+        return hipErrorInvalidDevice;
+    std::call_once(once[dev], [dev] {
+        void *a = nullptr;
+        err[dev] = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        addr[dev] = static_cast<uint32_t *>(a);
+    });
+    if (err[dev] != hipSuccess)
+        return err[dev];
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_fwd_bf16(const FwdParams &p, hipStream_t stream)
 {

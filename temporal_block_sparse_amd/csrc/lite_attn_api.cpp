@@ -11,6 +11,8 @@
 #include <cstring>
 #include <limits>
 
+static_assert(lite_attn::NOALLOC_SCHED_WORDS == LITE_ATTN_SCHED_WORDS, "one counter layout");
+
 namespace {
 
 thread_local char g_hip_msg[256] = "";
@@ -210,10 +212,13 @@ const char *lite_attn_strerror(int code)
     }
 }
 
-int lite_attn_fwd(const lite_attn_desc *desc, const void *q, const void *k, const void *v,
-                  const uint32_t *mask_in, uint32_t *mask_out, const int32_t *skiplist, float tau,
-                  float softmax_scale, void *out, float *lse, const lite_attn_ranges *ranges, uint32_t *sched,
-                  void *stream)
+namespace {
+
+// The forward behind both entry points: with own_sched the schedule counters
+// are the library's static per-device array (cleared first) instead of sched.
+int fwd_impl(const lite_attn_desc *desc, const void *q, const void *k, const void *v, const uint32_t *mask_in,
+             uint32_t *mask_out, const int32_t *skiplist, float tau, float softmax_scale, void *out, float *lse,
+             const lite_attn_ranges *ranges, uint32_t *sched, bool own_sched, void *stream)
 {
     Dims r;
     int rc = check_desc(desc, &r);
@@ -303,9 +308,37 @@ int lite_attn_fwd(const lite_attn_desc *desc, const void *q, const void *k, cons
                      p.rg.any, p.sched != nullptr, (double)tau);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (own_sched && desc->dtype == LITE_BF16) {
+        // the array keeps the last call's contents: clear the counters with
+        // a fill kernel (no memset, no allocation) before this call uses them
+        hipError_t e = lite_attn::noalloc_sched(&p.sched);
+        if (e == hipSuccess)
+            e = lite_attn::launch_reset_mask(p.sched, lite_attn::NOALLOC_SCHED_WORDS, s);
+        if (e != hipSuccess)
+            return hip_fail(e);
+    }
     const hipError_t e =
         desc->dtype == LITE_BF16 ? lite_attn::launch_fwd_bf16(p, s) : lite_attn::launch_fwd_fp32(p, s);
     return e == hipSuccess ? LITE_OK : hip_fail(e);
+}
+
+}  // namespace
+
+int lite_attn_fwd(const lite_attn_desc *desc, const void *q, const void *k, const void *v,
+                  const uint32_t *mask_in, uint32_t *mask_out, const int32_t *skiplist, float tau,
+                  float softmax_scale, void *out, float *lse, const lite_attn_ranges *ranges, uint32_t *sched,
+                  void *stream)
+{
+    return fwd_impl(desc, q, k, v, mask_in, mask_out, skiplist, tau, softmax_scale, out, lse, ranges, sched, false,
+                    stream);
+}
+
+int lite_attn_fwd_noalloc(const lite_attn_desc *desc, const void *q, const void *k, const void *v,
+                          const uint32_t *mask_in, uint32_t *mask_out, const int32_t *skiplist, float tau,
+                          float softmax_scale, void *out, float *lse, const lite_attn_ranges *ranges, void *stream)
+{
+    return fwd_impl(desc, q, k, v, mask_in, mask_out, skiplist, tau, softmax_scale, out, lse, ranges, nullptr, true,
+                    stream);
 }
 
 int lite_attn_build_skiplist(const lite_attn_desc *desc, const uint32_t *mask, int32_t *skiplist,

@@ -53,6 +53,9 @@ struct ErrParams {
 };
 
 hipError_t launch_fwd_bf16(const FwdParams &p, hipStream_t stream);
+// The library's own schedule counters on the current device (lite_attn_fwd_noalloc).
+constexpr int NOALLOC_SCHED_WORDS = 2;
+hipError_t noalloc_sched(uint32_t **ptr);
 hipError_t launch_fwd_fp32(const FwdParams &p, hipStream_t stream);
 hipError_t launch_build_skiplist(const uint32_t *mask, int32_t *skiplist, int64_t rows, int32_t Tk,
                                  const TileRanges &rg, hipStream_t stream);

@@ -28,7 +28,7 @@ MAX_MERGE_PARTS = 8
 ERRORS = {1: "LITE_ERR_NULL_ARG", 2: "LITE_ERR_BAD_SHAPE", 3: "LITE_ERR_UNSUPPORTED", 4: "LITE_ERR_BAD_THRESHOLD",
           5: "LITE_ERR_BAD_SCALE", 6: "LITE_ERR_MISALIGNED", 7: "LITE_ERR_ALIAS", 8: "LITE_ERR_HIP",
           9: "LITE_ERR_BAD_RANGES"}
-EXPORTS = ("lite_attn_fwd", "lite_attn_build_skiplist", "lite_attn_reset_mask", "lite_attn_merge",
+EXPORTS = ("lite_attn_fwd", "lite_attn_fwd_noalloc", "lite_attn_build_skiplist", "lite_attn_reset_mask", "lite_attn_merge",
            "lite_attn_error_sums", "lite_attn_mask_words", "lite_attn_skiplist_len", "lite_attn_strerror",
            "lite_attn_abi_version")
 
@@ -61,6 +61,8 @@ def _load():
     R = ctypes.POINTER(Ranges)
     lib.lite_attn_fwd.restype = ctypes.c_int
     lib.lite_attn_fwd.argtypes = [D, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float, P, P, R, P, P]
+    lib.lite_attn_fwd_noalloc.restype = ctypes.c_int
+    lib.lite_attn_fwd_noalloc.argtypes = [D, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float, P, P, R, P]
     lib.lite_attn_build_skiplist.restype = ctypes.c_int
     lib.lite_attn_build_skiplist.argtypes = [D, P, P, R, P]
     lib.lite_attn_reset_mask.restype = ctypes.c_int
@@ -220,6 +222,25 @@ def desc_of(q, tile_m, tile_n, k=None, out=None):
     return make_desc(B, N, H, D, tile_m, tile_n, q.dtype, Nk, qs, ks, os_)
 
 
+def _fwd_args(q, k, v, out, tile_m, tile_n, tau, softmax_scale, mask_in, mask_out, skiplist, lse, rg):
+    """The C forward's arguments up to its token ranges, checked."""
+    desc = desc_of(q, tile_m, tile_n, k, out)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(q.shape[-1])
+    if v.shape != k.shape or v.dtype != k.dtype or k.dtype != q.dtype:
+        raise ValueError("k and v must match, and share q's dtype")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if _bshd(v)[4] != desc.kv_batch_stride:
+        raise ValueError("v must be laid out like k")
+    mb = 4 * lite_attn_mask_words(desc)
+    return (ctypes.byref(desc), _bshd(q)[5], _bshd(k)[5], _bshd(v)[5], _buf(mask_in, mb, "mask_in"),
+            _buf(mask_out, mb, "mask_out"), _buf(skiplist, 4 * lite_attn_skiplist_len(desc), "skiplist"),
+            float(tau), float(softmax_scale), _bshd(out)[5],
+            _buf(lse, 4 * desc.batch * desc.heads * desc.seqlen, "lse", torch.float32),
+            ctypes.byref(rg) if rg is not None else None)
+
+
 def lite_attn_fwd(q, k, v, out, *, tile_m, tile_n, tau, softmax_scale=None, mask_in=None, mask_out=None,
                   skiplist=None, lse=None, must_do=None, must_skip=None, sched="auto", stream=None):
     """C lite_attn_fwd on BSHD tensors: q and out [B, Nq, H, d], k and v
@@ -232,27 +253,23 @@ def lite_attn_fwd(q, k, v, out, *, tile_m, tile_n, tau, softmax_scale=None, mask
     q-tile pair.  Raises LiteAttnError on a non-zero return code."""
     if isinstance(sched, str) and sched != "auto":
         raise ValueError('sched must be a tensor, "auto" or None')
-    desc = desc_of(q, tile_m, tile_n, k, out)
-    if softmax_scale is None:
-        softmax_scale = 1.0 / math.sqrt(q.shape[-1])
-    if v.shape != k.shape or v.dtype != k.dtype or k.dtype != q.dtype:
-        raise ValueError("k and v must match, and share q's dtype")
-    if out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("out must match q")
-    if _bshd(v)[4] != desc.kv_batch_stride:
-        raise ValueError("v must be laid out like k")
     rg = _ranges(must_do, must_skip)
-    mb = 4 * lite_attn_mask_words(desc)
+    args = _fwd_args(q, k, v, out, tile_m, tile_n, tau, softmax_scale, mask_in, mask_out, skiplist, lse, rg)
     st = _stream(stream)
     if isinstance(sched, str):
         sched = _sched_auto(st, q.device) if q.dtype == torch.bfloat16 and q.is_cuda else None
-    _check(LIB.lite_attn_fwd(ctypes.byref(desc), _bshd(q)[5], _bshd(k)[5], _bshd(v)[5],
-                             _buf(mask_in, mb, "mask_in"), _buf(mask_out, mb, "mask_out"),
-                             _buf(skiplist, 4 * lite_attn_skiplist_len(desc), "skiplist"), float(tau),
-                             float(softmax_scale), _bshd(out)[5],
-                             _buf(lse, 4 * desc.batch * desc.heads * desc.seqlen, "lse", torch.float32),
-                             ctypes.byref(rg) if rg is not None else None,
-                             _buf(sched, 4 * SCHED_WORDS, "sched", torch.int32), st))
+    _check(LIB.lite_attn_fwd(*args, _buf(sched, 4 * SCHED_WORDS, "sched", torch.int32), st))
+    return out
+
+
+def lite_attn_fwd_noalloc(q, k, v, out, *, tile_m, tile_n, tau, softmax_scale=None, mask_in=None,
+                          mask_out=None, skiplist=None, lse=None, must_do=None, must_skip=None, stream=None):
+    """C lite_attn_fwd_noalloc: lite_attn_fwd with the library's own schedule
+    counters (one static array per GPU; calls that overlap in time on one GPU
+    must not be made).  Neither the library nor this function allocates."""
+    rg = _ranges(must_do, must_skip)
+    args = _fwd_args(q, k, v, out, tile_m, tile_n, tau, softmax_scale, mask_in, mask_out, skiplist, lse, rg)
+    _check(LIB.lite_attn_fwd_noalloc(*args, _stream(stream)))
     return out
 
 

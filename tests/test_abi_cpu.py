@@ -153,6 +153,26 @@ def test_binding_schedule_argument():
         la._buf(torch.zeros(2, dtype=torch.int64), 4 * la.SCHED_WORDS, "sched", torch.int32)
 
 
+def fwd_noalloc(d, q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), mask_in=None, mask_out=None, skiplist=None,
+                tau=-3.0, scale=0.125, out=FAKE + (3 << 30), lse=None):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return la.LIB.lite_attn_fwd_noalloc(ctypes.byref(d) if d is not None else None, P(q), P(k), P(v),
+                                        P(mask_in), P(mask_out), P(skiplist), tau, scale, P(out), P(lse), None,
+                                        None)
+
+
+def test_noalloc_entry_point_validates_like_lite_attn_fwd():
+    """lite_attn_fwd_noalloc rejects what lite_attn_fwd rejects, with the same
+    codes, before it looks up its counters or touches the device."""
+    cases = [dict(d=None), dict(d=desc(tile_m=0)), dict(d=desc(head_dim=96)), dict(d=desc(), tau=float("nan")),
+             dict(d=desc(), scale=0.0), dict(d=desc(), q=None), dict(d=desc(), q=FAKE + 8),
+             dict(d=desc(), out=FAKE + 4096), dict(d=desc(seqlen=4097 * 128))]
+    for kw in cases:
+        want = fwd(**kw)
+        assert want != 0 and fwd_noalloc(**kw) == want, kw
+    assert fwd_noalloc(desc(seqlen=0), q=None, k=None, v=None, out=None) == 0
+
+
 def test_empty_descriptor_is_a_noop():
     for kw in (dict(seqlen=0), dict(batch=0), dict(heads=0)):
         assert fwd(desc(**kw), q=None, k=None, v=None, out=None) == 0
