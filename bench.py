@@ -306,6 +306,9 @@ def main():
                          "tokens x 32 heads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="only time plain bf16 GEMMs (torch.matmul, the vendor library): what a dense "
+                         "matrix-core kernel sustains on this GPU, for comparison with the forward")
     args = ap.parse_args()
 
     if args.steps < 1 or args.warmup < 0 or args.sweep_steps < 0:
@@ -323,6 +326,28 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4}))
+        return
+    if args.gemm_reference:
+        res = []
+        for m, n, k in ((8192, 8192, 8192), (16384, 16384, 8192), (32768, 8192, 8192)):
+            g = torch.Generator(device="cuda").manual_seed(0)
+            a = torch.randn(m, k, device="cuda", generator=g).to(torch.bfloat16)
+            b = torch.randn(k, n, device="cuda", generator=g).to(torch.bfloat16)
+            for _ in range(3):
+                c = a @ b
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                c = a @ b
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 20
+            tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+            res.append({"m": m, "n": n, "k": k, "ms": round(ms, 3), "tflops": round(tf, 1),
+                        "pct_mfma_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 1)})
+            log("[bench] gemm %dx%dx%d bf16: %.3f ms, %.0f TFLOP/s" % (m, n, k, ms, tf))
+            del a, b, c
+        print(json.dumps({"gemm_reference_bf16": res}))
         return
 
     from temporal_block_sparse_amd import configs, synth
