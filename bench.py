@@ -30,6 +30,10 @@ Printed (one JSON line on stdout):
                    LSE merge and the error sums at the workload's shape
   dense_variants   with --dense-variants: every bf16 kernel instantiation
                    (head_dim, key-tile width) dense at 32,768 tokens x 32 heads
+  pair_workload    default run only: the cond/uncond pair workload (batch 2,
+                   threshold schedule -10 .. 0), 5 timed steps after 3 warmups,
+                   with its own oracle check, run as a child process of this
+                   script (--no-pair skips it)
 
 --workload c1_fp32_1k measures the fp32 path instead (fp64 arithmetic on the
 fp64 matrix cores, against their 78.6 TFLOP/s peak).
@@ -247,6 +251,32 @@ def dense_variants(torch, la, N=32768, H=32):
     return res
 
 
+def pair_workload(args):
+    """The cond/uncond pair workload (batch 2, its threshold schedule), run
+    briefly as a child process of this script so that the default line also
+    records it: 5 timed steps after 3 warmups, with the oracle check of those
+    steps on 4 carried rows.  Returns a summary of the child's JSON line."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", "c5_bf16_76k_pair", "--steps", "5",
+           "--warmup", "3", "--sweep-steps", "0", "--cpu-rows", "4"]
+    if args.no_cpu:
+        cmd.append("--no-cpu")
+    log("[bench] pair workload: %s" % " ".join(cmd[1:]))
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=sys.stderr, text=True, timeout=900)
+    lines = [l for l in p.stdout.splitlines() if l.startswith("{")]
+    if p.returncode != 0 or not lines:
+        return {"error": "child exited with %d" % p.returncode, "command": " ".join(cmd[1:])}
+    j = json.loads(lines[-1])
+    v = j.get("verification") or {}
+    return {"command": "python bench.py " + " ".join(cmd[2:]), "value": j["value"], "unit": j["unit"],
+            "pct_mfma_peak": j["pct_mfma_peak"], "ms_per_step": j["ms_per_step"],
+            "speedup_vs_dense": j["speedup_vs_dense"], "dense_tflops": j["dense_tflops"],
+            "config": j["config"], "sparsity": j["sparsity"], "pair_occupancy": j["pair_occupancy"],
+            "roofline_frac": j["roofline"]["frac"],
+            "verification": {k: v.get(k) for k in ("within_bars", "max_abs_out", "max_lse", "mask_mismatch",
+                                                   "near_tau", "diverged_rows")} if v else None}
+
+
 def read_traffic(src_hash):
     """(bytes per launch, note) from the committed counter summary, or (None, why)."""
     if not os.path.exists(TRAFFIC_FILE):
@@ -306,6 +336,8 @@ def main():
                          "tokens x 32 heads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--no-pair", action="store_true",
+                    help="skip the short run of the cond/uncond pair workload that the default run adds")
     ap.add_argument("--gemm-reference", action="store_true",
                     help="only time plain bf16 GEMMs (torch.matmul, the vendor library): what a dense "
                          "matrix-core kernel sustains on this GPU, for comparison with the forward")
@@ -644,6 +676,8 @@ def main():
             "steps": checks}
 
     variants = dense_variants(torch, la) if args.dense_variants else None
+    pair = pair_workload(args) if (args.workload == "c4_bf16_76k" and not args.no_pair and not args.grid
+                                   and not args.heads and args.tau is None) else None
 
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -671,6 +705,7 @@ def main():
         "verification": verification,
         "tau_sweep": sweep,
         "dense_variants": variants,
+        "pair_workload": pair,
     }
     print(json.dumps(res), flush=True)
 
