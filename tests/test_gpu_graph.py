@@ -9,9 +9,10 @@ buffers, with eager work and a synchronisation between replays, and must give
 exactly what the eager calls give at the same step (every kernel here is
 deterministic: one workgroup per output row, no atomics on outputs).  A
 second graph captures reset + forward: eager calls between its replays grow
-the mask, and the captured reset has to clear it every time.  Last, two layers
+the mask, and the captured reset has to clear it every time.  Two layers
 stepping on two streams at once must match the same calls made one after the
-other.
+other.  Last, the bf16 forward with its schedule counters is replayed from a
+graph: the kernels reset the counters themselves, so no memset is captured.
 """
 
 import sys
@@ -125,3 +126,48 @@ def test_two_streams_equal_sequential_calls():
         for t in range(3):
             assert torch.equal(res[i][t][0], seq[i][t][0]), "layer %d step %d output" % (i, t)
             assert torch.equal(res[i][t][1], seq[i][t][1]), "layer %d step %d mask" % (i, t)
+
+
+def test_ticket_counters_inside_a_graph():
+    """The bf16 forward with caller-owned schedule counters, captured into a
+    graph: the kernels reset the counters themselves (no memset node), so
+    every replay -- with eager calls on the same counters in between --
+    draws its tickets from zero and gives the eager result, and the counters
+    read zero after each replay."""
+    wl = configs.scaled(configs.C3, (10, 30, 60), heads=4, batch=1, steps=3)  # 18,000 tokens: 284 pairs
+    steps = _steps(wl)
+    print("  N %d H %d pairs %d" % (wl.seqlen, wl.heads, wl.heads * ((wl.tq + 1) // 2)), flush=True)
+    counters = torch.zeros(la.SCHED_WORDS, dtype=torch.int32, device="cuda")
+    desc = la.desc_of(steps[0][0], wl.tile_m, wl.tile_n)
+    kw = dict(tile_m=wl.tile_m, tile_n=wl.tile_n, tau=-3.0)
+    # eager reference over the trajectory, mask carried
+    mask = torch.zeros(la.lite_attn_mask_words(desc), dtype=torch.int32, device="cuda")
+    eager = []
+    for q, k, v in steps:
+        o = torch.empty_like(q)
+        la.lite_attn_fwd(q, k, v, o, mask_in=mask, mask_out=mask, sched=counters, **kw)
+        eager.append((o, mask.clone()))
+    torch.cuda.synchronize()
+    assert counters.tolist() == [0, 0]
+    # capture one step with the same counters
+    qs, ks, vs = (t.clone() for t in steps[0])
+    out = torch.empty_like(qs)
+    gmask = torch.zeros_like(mask)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        la.lite_attn_fwd(qs, ks, vs, out, mask_in=gmask, mask_out=gmask, sched=counters, **kw)
+    for s, (q, k, v) in enumerate(steps):
+        qs.copy_(q)
+        ks.copy_(k)
+        vs.copy_(v)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager[s][0].view(torch.int16)), "replay %d output" % s
+        assert torch.equal(gmask, eager[s][1]), "replay %d mask" % s
+        assert counters.tolist() == [0, 0], "replay %d left counters %s" % (s, counters.tolist())
+        # an eager call on the same counters between replays
+        scratch = torch.empty_like(q)
+        la.lite_attn_fwd(q, k, v, scratch, sched=counters, **kw)
+        torch.cuda.synchronize()
+        assert counters.tolist() == [0, 0]
