@@ -11,10 +11,9 @@
 // passes, is marked in the mask carried to the next denoising step.
 //
 // Work decomposition
-// * The work unit is a pair of adjacent q-tiles (128 queries each) of one
-//   (batch, head), served by one workgroup of 8 wave64s: waves 0-3 the even
-//   q-tile "A", waves 4-7 the odd q-tile "B"; each wave owns 32 queries.  Wave
-//   w and wave w + 4 share a SIMD.
+// * One workgroup of 8 wave64s serves two adjacent q-tiles (128 queries each)
+//   of one (batch, head): waves 0-3 the even q-tile "A", waves 4-7 the odd
+//   q-tile "B"; each wave owns 32 queries.  Wave w and wave w + 4 share a SIMD.
 // * The workgroup walks the union of A's and B's live k-tiles in descending
 //   order, in steps of 64 keys.  A wave computes only the steps its own q-tile
 //   visits, so each q-tile sees exactly its own live tiles in its own order:
