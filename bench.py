@@ -60,6 +60,11 @@ KERNEL_SOURCES = {dt: [os.path.join(ROOT, "temporal_block_sparse_amd", "csrc", f
                   for dt, src in (("bf16", "fwd_bf16.hip"), ("fp32", "fwd_fp32.hip"))}
 
 
+# keyword arguments of every forward call: empty for the library's default
+# (the ticket schedule), {"sched": None} for one workgroup per q-tile pair
+FWD_KW = {}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -236,11 +241,11 @@ def dense_variants(torch, la, N=32768, H=32):
         o = torch.empty_like(q)
         sc = 1.0 / math.sqrt(D)
         for _ in range(2):
-            la.lite_attn_fwd(q, k, v, o, tile_m=128, tile_n=BN, tau=-math.inf, softmax_scale=sc)
+            la.lite_attn_fwd(q, k, v, o, tile_m=128, tile_n=BN, tau=-math.inf, softmax_scale=sc, **FWD_KW)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(5):
-            la.lite_attn_fwd(q, k, v, o, tile_m=128, tile_n=BN, tau=-math.inf, softmax_scale=sc)
+            la.lite_attn_fwd(q, k, v, o, tile_m=128, tile_n=BN, tau=-math.inf, softmax_scale=sc, **FWD_KW)
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / 5
@@ -258,7 +263,7 @@ def pair_workload(args):
     steps on 4 carried rows.  Returns a summary of the child's JSON line."""
     import subprocess
     cmd = [sys.executable, os.path.abspath(__file__), "--workload", "c5_bf16_76k_pair", "--steps", "5",
-           "--warmup", "3", "--sweep-steps", "0", "--cpu-rows", "4"]
+           "--warmup", "3", "--sweep-steps", "0", "--cpu-rows", "4", "--schedule", args.schedule]
     if args.no_cpu:
         cmd.append("--no-cpu")
     log("[bench] pair workload: %s" % " ".join(cmd[1:]))
@@ -336,6 +341,9 @@ def main():
                          "tokens x 32 heads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--schedule", choices=("tickets", "static"), default="tickets",
+                    help="bf16 forward schedule: persistent workgroups drawing q-tile pairs from ticket counters "
+                         "(the library's default), or one workgroup per pair")
     ap.add_argument("--no-pair", action="store_true",
                     help="skip the short run of the cond/uncond pair workload that the default run adds")
     ap.add_argument("--gemm-reference", action="store_true",
@@ -350,6 +358,8 @@ def main():
               "(the forward would shard by heads, each GPU running this kernel on its own heads).", file=sys.stderr)
         sys.exit(2)
 
+    if args.schedule == "static":
+        FWD_KW["sched"] = None
     import torch
     if args.copy_calibration:
         src = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
@@ -422,7 +432,7 @@ def main():
         if ev is not None:
             ev[0].record()
         la.lite_attn_fwd(q, k, v, out, tile_m=wl.tile_m, tile_n=wl.tile_n, tau=tau, softmax_scale=scale,
-                         mask_in=m_in, mask_out=m_out, skiplist=sl if m_in is not None else None)
+                         mask_in=m_in, mask_out=m_out, skiplist=sl if m_in is not None else None, **FWD_KW)
         if ev is not None:
             ev[1].record()
 
@@ -482,7 +492,8 @@ def main():
         q, k, v = inputs[t]
         ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
         ev[0].record()
-        la.lite_attn_fwd(q, k, v, out, tile_m=wl.tile_m, tile_n=wl.tile_n, tau=-math.inf, softmax_scale=scale)
+        la.lite_attn_fwd(q, k, v, out, tile_m=wl.tile_m, tile_n=wl.tile_n, tau=-math.inf, softmax_scale=scale,
+                         **FWD_KW)
         ev[1].record()
         dev_ms.append(ev)
     # The two mask kernels, 10 calls each, enqueued behind the dense launches:
@@ -531,7 +542,7 @@ def main():
             la.lite_attn_build_skiplist(desc, m_in, sl)
         la.lite_attn_fwd(q, k, v, ck_out, tile_m=wl.tile_m, tile_n=wl.tile_n, tau=tau, softmax_scale=scale,
                          mask_in=m_in, mask_out=ck_mask if m_in is not None else None,
-                         skiplist=sl if m_in is not None else None, lse=ck_lse)
+                         skiplist=sl if m_in is not None else None, lse=ck_lse, **FWD_KW)
         torch.cuda.synchronize()
         c = chk.compare(label, t, tau, ck_out, ck_lse, m_in, ck_mask if m_in is not None else None)
         if m_timed is not None:
@@ -588,7 +599,8 @@ def main():
                 ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 if tau is not None and math.isinf(tau):
                     ev[0].record()
-                    la.lite_attn_fwd(q, k, v, out, tile_m=wl.tile_m, tile_n=wl.tile_n, tau=tau, softmax_scale=scale)
+                    la.lite_attn_fwd(q, k, v, out, tile_m=wl.tile_m, tile_n=wl.tile_n, tau=tau, softmax_scale=scale,
+                                     **FWD_KW)
                     ev[1].record()
                     pend.append((tau, ev, None))
                 else:
@@ -685,7 +697,8 @@ def main():
         "dtype": "bf16" if bf16 else "fp64", "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "seq_len": wl.seqlen,
                    "grid": list(wl.grid), "head_dim": wl.head_dim, "tile": "%dx%d" % (wl.tile_m, wl.tile_n),
-                   "tau": tau_desc, "path": args.path, "timed_steps": [W, W + K - 1]},
+                   "tau": tau_desc, "path": args.path, "timed_steps": [W, W + K - 1],
+                   "schedule": args.schedule if bf16 else None},
         "pct_mfma_peak": round(100.0 * value / peak, 2),
         "speedup_vs_dense": round(sum(dense_ms) / sum(kern_ms), 3),
         "dense_kernel_ms": round(sum(dense_ms) / K, 3), "kernel_ms": round(sum(kern_ms) / K, 3),
