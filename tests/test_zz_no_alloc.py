@@ -54,3 +54,21 @@ def test_noalloc_entry_point_matches_lite_attn_fwd(use_skiplist):
                 a, b = a.view(torch.int16), b.view(torch.int16)
             assert torch.equal(a, b), (i, name)
         assert counters.tolist() == [0, 0]
+
+
+def test_noalloc_entry_point_fp32_path():
+    """The fp32 forward has no schedule counters: through the allocation-free
+    entry point it is the same call, bit for bit."""
+    dev = torch.device("cuda")
+    q, k, v = synth.random_qkv(1, 700, 2, 64, dtype=torch.float32, seed=80, scale=2.0, device=dev)
+    mask_in = synth.random_mask(2 * 11, 11, 0.4, seed=81).to(dev)
+    outs = []
+    for fn in (la.lite_attn_fwd, la.lite_attn_fwd_noalloc):
+        out = torch.empty_like(q)
+        lse = torch.empty(1, 2, 700, dtype=torch.float32, device=dev)
+        mask_out = torch.empty_like(mask_in)
+        fn(q, k, v, out, tile_m=64, tile_n=64, tau=-2.0, mask_in=mask_in, mask_out=mask_out, lse=lse)
+        outs.append((out, lse, mask_out))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
