@@ -107,3 +107,48 @@ def test_binding_keeps_one_buffer_per_stream():
     assert b1.tolist() == [0, 0] and b2.tolist() == [0, 0]
     for o in outs:
         assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+
+
+def _random_cases(n, seed):
+    g = torch.Generator().manual_seed(seed)
+    r = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=g))  # noqa: E731
+    cases = []
+    for i in range(n):
+        B, d, tile_n = r(1, 2), (64, 128)[r(0, 1)], (64, 128)[r(0, 1)]
+        N, H = r(2000, 9000), r(4, 16)
+        pph = (-(-N // 128) + 1) // 2                 # q-tile pairs per (batch entry, head)
+        H = max(H, -(-300 // (B * pph)))              # at least 300 pairs: more than the CUs
+        tk = -(-N // tile_n)
+        rg = {}
+        if r(0, 2) == 0:   # token ranges on a third of the cases
+            a = r(N // 2, N - 1)
+            rg = dict(must_do=[N - 1, N - 1 - r(1, 300)], must_skip=[a, a - r(1, 2000)])
+            if rg["must_skip"][1] < -1 or rg["must_skip"][0] >= rg["must_do"][1]:
+                rg = dict(must_do=rg["must_do"])
+        cases.append((B, N, H, d, tile_n, -0.5 * r(0, 10), bool(r(0, 1)), rg, 0.1 * r(0, 9), tk))
+    return cases
+
+
+@pytest.mark.parametrize("i,case", list(enumerate(_random_cases(12, 2024))))
+def test_random_shapes_with_several_pairs_per_workgroup(i, case):
+    """Seeded shapes whose launches hold more q-tile pairs than the GPU has
+    compute units, so persistent workgroups draw several tickets each; ragged
+    last tiles, odd q-tile counts (a last pair with one q-tile), batch 2,
+    token ranges.  The ticket schedule must equal one workgroup per pair bit
+    for bit (that path is held to the oracle by the parity tests)."""
+    B, N, H, d, tile_n, tau, use_skiplist, rg, density, tk = case
+    dev = torch.device("cuda")
+    tq = -(-N // 128)
+    log("  case %d: B=%d N=%d H=%d d=%d tile 128x%d tau %g skiplist %s ranges %s density %.1f pairs %d"
+        % (i, B, N, H, d, tile_n, tau, use_skiplist, rg, density, B * H * ((tq + 1) // 2)))
+    q, k, v = synth.random_qkv(B, N, H, d, dtype=torch.bfloat16, seed=100 + i, scale=2.0, device=dev)
+    mask_in = synth.random_mask(B * H * tq, tk, density, seed=200 + i).to(dev)
+    counters = torch.zeros(la.SCHED_WORDS, dtype=torch.int32, device=dev)
+    ref = run(q, k, v, tile_n, tau, mask_in, use_skiplist, rg, None)
+    got = run(q, k, v, tile_n, tau, mask_in, use_skiplist, rg, counters)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("out", "lse", "mask_out"), ref, got):
+        if a.dtype == torch.bfloat16:
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        assert torch.equal(a, b), (i, name)
+    assert counters.tolist() == [0, 0]
