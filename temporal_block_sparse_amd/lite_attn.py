@@ -194,19 +194,29 @@ def _ranges(must_do, must_skip):
 _SCHED = {}
 
 
-def _sched_auto(stream_handle, device):
+def _torch_stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream))
+
+
+def _sched_auto(stream, device):
     """The counters for calls on this stream, or None (one workgroup per pair)
-    while the current stream is being captured into a graph: a graph replayed
-    on another stream could then run at the same time as eager calls sharing
-    the buffer."""
-    key = (device.index, stream_handle.value or 0)
-    buf = _SCHED.get(key)
-    if buf is None:
+    while the stream is being captured into a graph: a graph replayed on
+    another stream could then run at the same time as eager calls sharing
+    the buffer.  A new buffer is zeroed by a fill kernel on the stream itself,
+    ahead of the forward that uses it, so no synchronisation is needed."""
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
         if torch.cuda.is_current_stream_capturing():
             return None
-        buf = torch.zeros(SCHED_WORDS, dtype=torch.int32, device=device)
-        torch.cuda.synchronize(device)  # zero before any stream uses it
-        _SCHED[key] = buf
+        key = (device.index, ts.cuda_stream)
+        buf = _SCHED.get(key)
+        if buf is None:
+            buf = torch.zeros(SCHED_WORDS, dtype=torch.int32, device=device)
+            _SCHED[key] = buf
     return buf
 
 
@@ -257,7 +267,7 @@ def lite_attn_fwd(q, k, v, out, *, tile_m, tile_n, tau, softmax_scale=None, mask
     args = _fwd_args(q, k, v, out, tile_m, tile_n, tau, softmax_scale, mask_in, mask_out, skiplist, lse, rg)
     st = _stream(stream)
     if isinstance(sched, str):
-        sched = _sched_auto(st, q.device) if q.dtype == torch.bfloat16 and q.is_cuda else None
+        sched = _sched_auto(stream, q.device) if q.dtype == torch.bfloat16 and q.is_cuda else None
     _check(LIB.lite_attn_fwd(*args, _buf(sched, 4 * SCHED_WORDS, "sched", torch.int32), st))
     return out
 
