@@ -171,3 +171,32 @@ def test_ticket_counters_inside_a_graph():
         la.lite_attn_fwd(q, k, v, scratch, sched=counters, **kw)
         torch.cuda.synchronize()
         assert counters.tolist() == [0, 0]
+
+
+def test_binding_captures_without_counters_on_a_stream_that_has_them():
+    """A stream whose eager calls already use the binding's counter buffer is
+    then captured: while it captures, the binding passes no counters, so the
+    graph holds the one-workgroup-per-pair launch and shares nothing with the
+    eager calls.  Replays equal the eager result."""
+    wl = configs.scaled(configs.C3, (10, 30, 60), heads=4, batch=1, steps=2)
+    (q, k, v), _ = _steps(wl)
+    s = torch.cuda.Stream()
+    ref = torch.empty_like(q)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        la.lite_attn_fwd(q, k, v, ref, tile_m=wl.tile_m, tile_n=wl.tile_n, tau=-3.0)
+    s.synchronize()
+    di = torch.cuda.current_device()
+    assert (di, s.cuda_stream) in la._SCHED          # the stream has its counters
+    out = torch.empty_like(q)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        la.lite_attn_fwd(q, k, v, out, tile_m=wl.tile_m, tile_n=wl.tile_n, tau=-3.0)
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+        with torch.cuda.stream(s):                     # eager calls on the same stream in between
+            la.lite_attn_fwd(q, k, v, ref, tile_m=wl.tile_m, tile_n=wl.tile_n, tau=-3.0)
+        s.synchronize()
+    assert la._SCHED[(di, s.cuda_stream)].tolist() == [0, 0]
