@@ -267,7 +267,10 @@ def pair_workload(args):
     if args.no_cpu:
         cmd.append("--no-cpu")
     log("[bench] pair workload: %s" % " ".join(cmd[1:]))
-    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=sys.stderr, text=True, timeout=900)
+    try:
+        p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=sys.stderr, text=True, timeout=900)
+    except subprocess.TimeoutExpired:
+        return {"error": "child timed out after 900 s", "command": " ".join(cmd[1:])}
     lines = [l for l in p.stdout.splitlines() if l.startswith("{")]
     if p.returncode != 0 or not lines:
         return {"error": "child exited with %d" % p.returncode, "command": " ".join(cmd[1:])}
