@@ -22,6 +22,7 @@ halves).
 """
 
 import math
+import os
 import sys
 
 import numpy as np
@@ -137,12 +138,15 @@ def test_c3_trajectory_full_size(use_skiplist):
 def test_c4_trajectory_full_size(tau):
     """75,600 tokens x 40 heads on the Skip-List walk the benchmark times, 10
     steps at each finite threshold of the sweep: 16 rows every step, 128 rows
-    at steps 0 and 1."""
+    at steps 0 and 1.  With LITE_ATTN_FULL_TRAJECTORIES=1 in the environment,
+    all 50 steps of the sweep's trajectories (about 2.5 minutes each at
+    tau = 0, too long for the default run)."""
     wl = configs.C4
+    steps = wl.steps if os.environ.get("LITE_ATTN_FULL_TRAJECTORIES") == "1" else 10
     big = pa.sample_rows_in_heads(wl.batch, wl.heads, wl.tq, 128, 8, seed=41)
     small = big[np.random.default_rng(2).choice(len(big), 16, replace=False)]
     small = np.unique(np.concatenate([small, big[[0, -1]]]))
-    stats = run_full_trajectory(wl, lambda t: tau, 10, small, big, big_steps=(0, 1))
+    stats = run_full_trajectory(wl, lambda t: tau, steps, small, big, big_steps=(0, 1))
     if tau >= -3.0:
         assert stats[-1]["sparsity"] > 0.1
 
