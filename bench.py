@@ -69,11 +69,40 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(dtype="bf16"):
+def strip_code(text):
+    """C++ source with its comments removed, each line's blank space collapsed
+    and empty lines dropped: what a comment or layout edit leaves unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":                 # a literal: copied whole, escapes included
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    lines = (" ".join(ln.split()) for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
+def kernel_code_hash(dtype="bf16"):
+    """First 16 hex digits of the sha256 of the kernel's sources with comments
+    and blank space removed: counters taken on one build stay valid across
+    edits of its comments, and lapse with any change to the code."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[dtype]:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(strip_code(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -285,7 +314,7 @@ def pair_workload(args):
                                                    "near_tau", "diverged_rows")} if v else None}
 
 
-def read_traffic(src_hash):
+def read_traffic(code_hash):
     """(bytes per launch, note) from the committed counter summary, or (None, why)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None, "no counter summary"
@@ -294,7 +323,7 @@ def read_traffic(src_hash):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != src_hash:
+    if kv.get("kernel_code_sha256_16") != code_hash:
         return None, "kernel changed since the counters were taken"
     try:
         return float(kv["hbm_bytes_per_launch"]), kv.get("note", "")
@@ -567,9 +596,9 @@ def main():
 
     value = sum(flops) / wall / 1e12
     achieved = sum(flops) / (sum(kern_ms) * 1e-3) / 1e12
-    src_hash = kernel_source_hash(wl.dtype)
+    code_hash = kernel_code_hash(wl.dtype)
     if bf16 and wl.name == "c4_bf16_76k":
-        traffic, traffic_note = read_traffic(src_hash)
+        traffic, traffic_note = read_traffic(code_hash)
     else:
         traffic, traffic_note = None, "the committed counter summary covers the 75,600-token bf16 workload only"
     sparsity = [1.0 - f / dense_flops for f in flops]
@@ -716,7 +745,7 @@ def main():
                      "kernel": ("fwd_bf16_kernel<%d, %d, %s>" % (wl.head_dim, wl.tile_n,
                                                                   "true" if args.path == "skiplist" else "false"))
                      if bf16 else "fwd_fp32_kernel",
-                     "kernel_source_sha256_16": src_hash},
+                     "kernel_code_sha256_16": code_hash},
         "cpu_baseline": cpu,
         "verification": verification,
         "tau_sweep": sweep,

@@ -11,9 +11,10 @@
 // passes, is marked in the mask carried to the next denoising step.
 //
 // Work decomposition
-// * One workgroup of 8 wave64s serves two adjacent q-tiles (128 queries each)
-//   of one (batch, head): waves 0-3 the even q-tile "A", waves 4-7 the odd
-//   q-tile "B"; each wave owns 32 queries.  Wave w and wave w + 4 share a SIMD.
+// * The work unit is a pair of adjacent q-tiles (128 queries each) of one
+//   (batch, head), served by one workgroup of 8 wave64s: waves 0-3 the even
+//   q-tile "A", waves 4-7 the odd q-tile "B"; each wave owns 32 queries.  Wave
+//   w and wave w + 4 share a SIMD.
 // * The workgroup walks the union of A's and B's live k-tiles in descending
 //   order, in steps of 64 keys.  A wave computes only the steps its own q-tile
 //   visits, so each q-tile sees exactly its own live tiles in its own order:
@@ -258,11 +259,8 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2, int npairs)
         vr0 = lr;
         vc0 = (pos ^ v_swz<D>(lr)) * 16;
     }
-    // The loads of one step into one LDS stage.  Instruction i covers key rows
-    // [key0 + i*RPI, +RPI): its buffer starts at row key0 + i*RPI and spans the
-    // rows of that block that exist, so rows past the end of the sequence read
-    // as zeros (their logits are set to -inf before use) and no address leaves
-    // the tensors.  All of it is scalar arithmetic.
+    // LDS destinations (M0) of this wave's DMA slots, and each lane's byte
+    // offset within a step's rows of K and V.
     const uint32_t m0_k = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)LDS_VOID(kbuf) + wq * 64 * 16);
     const uint32_t m0_v = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)LDS_VOID(vbuf) + wq * 64 * 16);
     uint32_t koff = (uint32_t)(kr0 * rs2_0 + kc0);
@@ -350,6 +348,11 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2, int npairs)
             qf[ds] = __builtin_bit_cast(bf16x8, x);
         }
 
+        // The loads of one step into one LDS stage.  Instruction i covers key rows
+        // [key0 + i*RPI, +RPI): its buffer starts at row key0 + i*RPI and spans the
+        // rows of that block that exist, so rows past the end of the sequence read
+        // as zeros (their logits are set to -inf before use) and no address leaves
+        // the tensors.  All of it is scalar arithmetic.
         struct DmaPlan {
             const char *kb, *vb;
             int st;
@@ -725,7 +728,7 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2, int npairs)
         else
             run(std::integral_constant<int, 1>{});
         __builtin_amdgcn_s_waitcnt(WAIT_ALL);
-        __syncthreads();  // every load landed before the workgroup's LDS is released
+        __syncthreads();  // every load landed before the next pair reuses the stages (or the LDS is released)
 
         // ---- epilogue ----
         const float l_tot = l_run + other_half(l_run);

@@ -186,3 +186,30 @@ def test_trajectory_tensors_are_snapshots():
         tr.advance()
         assert torch.equal(q, q0)
         assert not torch.equal(tr.tensors()[0], q0)
+
+
+def test_code_hash_ignores_comments_and_layout_only():
+    """The counter summaries are tied to the kernel's code: a comment or
+    indentation edit keeps the hash, any change to code or to a literal
+    changes it."""
+    src = ('#include "a.h"  // header\n'
+           '/* block\n   comment */ int f(int x) {\n'
+           '    asm volatile("s_nop 0 // not a comment");\n'
+           "    char c = '\"'; // a quote in a char literal\n"
+           '    return x + 1;\n}\n')
+    base = bench.strip_code(src)
+    assert "block" not in base and "header" not in base
+    assert '"s_nop 0 // not a comment"' in base and "'\"'" in base
+    same = [src.replace("// header", "// the header, reworded"),
+            src.replace("    return", "\t\treturn"),
+            src.replace("/* block\n   comment */", "/* one line */"),
+            src + "\n\n// trailing note\n"]
+    for s in same:
+        assert bench.strip_code(s) == base, s
+    changed = [src.replace("x + 1", "x + 2"),
+               src.replace("s_nop 0", "s_nop 1"),
+               src.replace("int f", "long f")]
+    for s in changed:
+        assert bench.strip_code(s) != base, s
+    assert len(bench.kernel_code_hash("bf16")) == 16
+    assert bench.kernel_code_hash("bf16") != bench.kernel_code_hash("fp32")
