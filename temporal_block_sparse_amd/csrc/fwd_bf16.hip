@@ -152,11 +152,16 @@ struct Step {
 // the end of the sequence are handled.  Issued from an asm block: the compiler
 // does not count these loads, so it never delays an LDS read for them; the
 // kernel waits for them explicitly (vmcnt) before the barriers that publish a
-// stage and before it exits.  The leading s_nop covers the wait states an
-// M0 or SGPR write needs before a buffer load reads it.
+// stage and before it exits.  The compiler's hazard recognizer does not look
+// into the asm either: the leading s_nop is the one wait state a load to LDS
+// needs after a scalar write of M0 (the rule the compiler applies to its own
+// such loads).  The longer wait after a vector write of an SGPR the load
+// reads (v_readlane, v_readfirstlane) is not provided: the code built here
+// has no such write within that distance of any of these loads, which a test
+// checks on the disassembled library over every path.
 __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t off, uint32_t l)
 {
-    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(l));
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(l));
 }
 
 __device__ __forceinline__ const char *uniform_ptr(const char *x)
