@@ -265,12 +265,17 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2, int npairs)
         vc0 = (pos ^ v_swz<D>(lr)) * 16;
     }
     // LDS destinations (M0) of this wave's DMA slots, and each lane's byte
-    // offset within a step's rows of K and V.
+    // offsets within a step's rows of K and V, one per load instruction (held
+    // in registers for the whole kernel, so that a load adds no vector work).
     const uint32_t m0_k = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)LDS_VOID(kbuf) + wq * 64 * 16);
     const uint32_t m0_v = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)LDS_VOID(vbuf) + wq * 64 * 16);
-    uint32_t koff = (uint32_t)(kr0 * rs2_0 + kc0);
-    uint32_t voff = (uint32_t)(vr0 * rs2_0 + vc0);
-    asm volatile("" : "+v"(koff), "+v"(voff));
+    uint32_t koff[G::IPA], voff[G::IPA];
+#pragma unroll
+    for (int i = 0; i < G::IPA; ++i) {
+        koff[i] = (uint32_t)((kr0 + i * G::RPI) * rs2_0 + kc0);
+        voff[i] = (uint32_t)((vr0 + i * G::RPI) * rs2_0 + vc0);
+        asm volatile("" : "+v"(koff[i]), "+v"(voff[i]));
+    }
     // This lane's slot as a source of the transposed V read: key row 8g + a of
     // the 16-key group, 4 head-dim entries starting at sigma(16*(lane/16 % 2) + 4b),
     // where lane % 16 = 4a + b.  The lane that receives column i of a 32-entry
@@ -353,39 +358,34 @@ fwd_bf16_kernel(FwdParams p, float c2, float tau2, int npairs)
             qf[ds] = __builtin_bit_cast(bf16x8, x);
         }
 
-        // The loads of one step into one LDS stage.  Instruction i covers key rows
-        // [key0 + i*RPI, +RPI): its buffer starts at row key0 + i*RPI and spans the
-        // rows of that block that exist, so rows past the end of the sequence read
-        // as zeros (their logits are set to -inf before use) and no address leaves
-        // the tensors.  All of it is scalar arithmetic.
+        // The loads of one step into one LDS stage.  One buffer per tensor and
+        // step starts at row key0 and spans the step's rows that exist; instruction
+        // i covers rows [key0 + i*RPI, +RPI) through the lane's offsets koff[i] /
+        // voff[i].  The range check applies to those offsets, so rows past the end
+        // of the sequence read as zeros (their logits are set to -inf before use)
+        // and no address leaves the tensors.  Building the two buffers is a few
+        // scalar instructions per step; each load then needs only its M0.
         struct DmaPlan {
-            const char *kb, *vb;
-            int st;
-            int bytes;  // bytes of the step's rows that exist: min(Nk - key0, HK) rows
+            u32x4 kr, vr;    // buffers over the step's rows that exist: min(Nk - key0, HK) rows
+            uint32_t mk, mv; // LDS destinations of the stage's first instruction
         };
         auto plan_step = [&](int key0, int st) __attribute__((always_inline)) {
             DmaPlan d;
-            d.st = st;
-            d.kb = Kb + (int64_t)key0 * rs2;
-            d.vb = Vb + (int64_t)key0 * rs2;
-            d.bytes = min(Nk - key0, HK) * rs2;
+            const uint32_t bytes = (uint32_t)(min(Nk - key0, HK) * rs2);
+            d.kr = buffer_rsrc(Kb + (int64_t)key0 * rs2, bytes);
+            d.vr = buffer_rsrc(Vb + (int64_t)key0 * rs2, bytes);
+            // this wave's bases, made opaque once per step so that the compiler
+            // adds the stage and instruction offsets in the loop instead of
+            // keeping one precomputed scalar per (stage, instruction) live
+            uint32_t kb0 = m0_k, vb0 = m0_v;
+            asm volatile("" : "+s"(kb0), "+s"(vb0));
+            d.mk = kb0 + (uint32_t)(st * G::CH * 16);
+            d.mv = vb0 + (uint32_t)(st * G::CH * 16);
             return d;
         };
         auto issue_dma = [&](const DmaPlan &d, int i) __attribute__((always_inline)) {
-            // bytes of instruction i's RPI rows that exist; max(x, 0) as a sign
-            // mask keeps the clamp in scalar instructions
-            int x = d.bytes - i * G::RPI * rs2;
-            x &= ~(x >> 31);
-            const uint32_t bytes = (uint32_t)min(x, G::RPI * rs2);
-            const int64_t blk = (int64_t)i * G::RPI * rs2;
-            // LDS destinations: this wave's base, made opaque so that the compiler
-            // adds the stage/instruction offset here instead of keeping one
-            // precomputed scalar per (stage, instruction) live across the loop
-            uint32_t kb0 = m0_k, vb0 = m0_v;
-            asm volatile("" : "+s"(kb0), "+s"(vb0));
-            const uint32_t o = (uint32_t)(d.st * G::CH * 16 + i * 4 * 64 * 16);
-            dma16(buffer_rsrc(d.kb + blk, bytes), koff, kb0 + o);
-            dma16(buffer_rsrc(d.vb + blk, bytes), voff, vb0 + o);
+            dma16(d.kr, koff[i], d.mk + (uint32_t)(i * 4 * 64 * 16));
+            dma16(d.vr, voff[i], d.mv + (uint32_t)(i * 4 * 64 * 16));
         };
 
         f32x16 O[D / 32];
