@@ -56,14 +56,15 @@
 //   halves in step u, its V by both halves in step u + 1), step u + 1 is in
 //   flight and A's waves issue step u + 2 among their QK^T MFMAs.  The four
 //   stages' K share one LDS array and their V another, so each LDS read
-//   address is a per-lane register computed once plus an immediate.  Each
-//   load's source is a buffer resource (base, byte range) built in scalar
-//   registers per 16 or 32 key rows, so addresses cost no vector
-//   instructions, and rows past the end of the sequence read as zeros through
-//   the range check instead of being clamped.  The loads are issued from asm
-//   blocks, which keeps the compiler from making LDS reads of other stages
-//   wait for them; explicit vmcnt waits publish a stage at the barrier that
-//   ends the step before its first use.
+//   address is a per-lane register computed once plus an immediate.  A
+//   step's loads read one buffer resource (base, byte range) per tensor,
+//   built in scalar registers once per step; each lane reaches its row and
+//   chunk through a per-instruction offset register computed once, so a load
+//   costs no vector instruction, and rows past the end of the sequence read
+//   as zeros through the range check instead of being clamped.  The loads are
+//   issued from asm blocks, which keeps the compiler from making LDS reads of
+//   other stages wait for them; explicit vmcnt waits publish a stage at the
+//   barrier that ends the step before its first use.
 // * K rows sit in LDS with rows 4..7 and 8..11 of every 16 swapped, so the 8
 //   scores a lane holds per 16-key MFMA step are 8 consecutive keys.  V stays
 //   in natural (key x head-dim) layout and the PV A-operand (V^T) is read with
