@@ -99,7 +99,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
-#define LDS_S16X4(p) ((__attribute__((address_space(3))) s16x4 *)(p))
 #define LDS_VOID(p) ((__attribute__((address_space(3))) void *)(p))
 
 constexpr int BM = 128;       // queries per q-tile
