@@ -202,16 +202,21 @@ def test_empty_sequence_is_noop():
     la.lite_attn_fwd(q, q.clone(), q.clone(), out, tile_m=128, tile_n=128, tau=-3.0)
 
 
-def test_maximum_k_tiles():
-    """Tk = 4096 (524,288 tokens, 128 mask words per row) with 95% of tiles skipped."""
-    N, H, D = 4096 * 128, 1, 128
+@pytest.mark.parametrize("D,BN,skiplist", [(128, 128, False), (128, 128, True), (64, 64, True), (64, 128, False)])
+def test_maximum_k_tiles(D, BN, skiplist):
+    """Tk = 4096 (128 mask words per row: 524,288 tokens at 128-key tiles,
+    262,144 at 64-key tiles) with 95% of tiles skipped, on both walks and
+    both head dims; rows at the start, middle and end."""
+    N, H = 4096 * BN, 1
+    log("  bf16 N %d d %d tile 128x%d skiplist %s" % (N, D, BN, skiplist))
     q, k, v = synth.random_qkv(1, N, H, D, torch.bfloat16, seed=1, scale=1.0, device="cuda")
     Tq = N // 128
     mask = synth.random_mask(H * Tq, 4096, 0.95, seed=11).numpy()
     rows = np.array([0, Tq // 2, Tq - 1], np.int64)
-    gpu = pa.gpu_fwd(q, k, v, 128, 128, -3.0, 0.088, mask_in=mask)
-    orc = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), 128, 128, -3.0, 0.088, mask_in=mask, rows=rows)
-    pa.compare_rows(gpu, orc, rows, 1, N, H, 128, 128, -3.0, torch.bfloat16)
+    scale = 1.0 / math.sqrt(D)
+    gpu = pa.gpu_fwd(q, k, v, 128, BN, -3.0, scale, mask_in=mask, use_skiplist=skiplist)
+    orc = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), 128, BN, -3.0, scale, mask_in=mask, rows=rows)
+    log("  ", pa.compare_rows(gpu, orc, rows, 1, N, H, 128, BN, -3.0, torch.bfloat16))
 
 
 @pytest.mark.parametrize("N,density,skiplist", [(4096 * 64 - 17, 0.95, False), (4096 * 64 - 17, 0.95, True),
