@@ -14,7 +14,10 @@ Printed (one JSON line on stdout):
   roofline         dominant kernel (the forward): algorithmic flops per launch
                    / HIP-event launch duration, against the bf16 MFMA peak;
                    traffic from the committed rocprofv3 counter summary when
-                   it was taken on the current kernel source, else null
+                   it was taken on the current kernel code, else null; likewise
+                   clock_ghz, the sustained clock of that counter run's timed
+                   launches, and frac_at_clock, the fraction of the peak at
+                   that clock (the chip runs power-limited below 2.4 GHz)
   cpu_baseline     the CPU oracle timed on a bounded sample of the same
                    trajectory: a fixed set of rows (one per host thread, at
                    most 16) that the oracle carries from an empty mask through
@@ -55,6 +58,9 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_FP64_TFLOPS = 78.6   # fp64 matrix (and vector) peak: the fp32 path computes in fp64
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_c4_76k.txt")
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_utilisation_fwd_bf16_c4_76k.txt")
+PMC_NOTE = ("mean sustained clock of the timed masked launches in the committed counter run of this code "
+            "(GRBM_GUI_ACTIVE / 8 / duration), not measured in this run; frac_at_clock = achieved / (peak x clock / 2.4 GHz)")
 KERNEL_SOURCES = {dt: [os.path.join(ROOT, "temporal_block_sparse_amd", "csrc", f)
                       for f in (src, "lite_attn_internal.h")]
                   for dt, src in (("bf16", "fwd_bf16.hip"), ("fp32", "fwd_fp32.hip"))}
@@ -331,6 +337,31 @@ def read_traffic(code_hash):
         return None, "malformed counter summary"
 
 
+def read_clock(code_hash):
+    """(GHz, note): the sustained clock of the timed masked launches in the
+    committed utilisation-counter summary (GRBM_GUI_ACTIVE over each launch's
+    duration), or (None, why).  The first skip-list dispatch there is the
+    warmup step; the rest are timed steps.  Like the traffic figure it is
+    taken from a counter run of the same code, not from this run."""
+    if not os.path.exists(PMC_FILE):
+        return None, "no counter summary"
+    ghz, code = [], None
+    for line in open(PMC_FILE):
+        if line.startswith("kernel_code_sha256_16:"):
+            code = line.split(":", 1)[1].strip()
+        f = line.split()
+        if len(f) >= 8 and f[0].isdigit() and "true>" in line and "skip-list" in line:
+            try:
+                ghz.append(float(f[f.index("skip-list") + 2]))
+            except (ValueError, IndexError):
+                return None, "malformed counter summary"
+    if code != code_hash:
+        return None, "kernel changed since the counters were taken"
+    if len(ghz) < 2:
+        return None, "malformed counter summary"
+    return sum(ghz[1:]) / len(ghz[1:]), PMC_NOTE
+
+
 def cpu_threads():
     n = os.environ.get("OMP_NUM_THREADS")
     try:
@@ -597,10 +628,13 @@ def main():
     value = sum(flops) / wall / 1e12
     achieved = sum(flops) / (sum(kern_ms) * 1e-3) / 1e12
     code_hash = kernel_code_hash(wl.dtype)
-    if bf16 and wl.name == "c4_bf16_76k":
+    if bf16 and wl.name == "c4_bf16_76k" and args.path == "skiplist":
         traffic, traffic_note = read_traffic(code_hash)
+        clock, clock_note = read_clock(code_hash)
     else:
-        traffic, traffic_note = None, "the committed counter summary covers the 75,600-token bf16 workload only"
+        traffic, traffic_note = None, ("the committed counter summaries cover the 75,600-token bf16 workload "
+                                       "on the Skip-List walk only")
+        clock, clock_note = None, traffic_note
     sparsity = [1.0 - f / dense_flops for f in flops]
     occupancy = [pair_occupancy(masks[t], wl) for t in range(K)]
 
@@ -742,6 +776,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
                      "traffic": traffic, "traffic_note": traffic_note,
+                     "clock_ghz": round(clock, 3) if clock else None,
+                     "frac_at_clock": round(achieved / (peak * clock / 2.4), 4) if clock else None,
+                     "clock_note": clock_note,
                      "kernel": ("fwd_bf16_kernel<%d, %d, %s>" % (wl.head_dim, wl.tile_n,
                                                                   "true" if args.path == "skiplist" else "false"))
                      if bf16 else "fwd_fp32_kernel",

@@ -213,3 +213,24 @@ def test_code_hash_ignores_comments_and_layout_only():
         assert bench.strip_code(s) != base, s
     assert len(bench.kernel_code_hash("bf16")) == 16
     assert bench.kernel_code_hash("bf16") != bench.kernel_code_hash("fp32")
+
+
+def test_profiled_clock_reader(tmp_path, monkeypatch):
+    """The clock reported next to the roofline comes from the committed counter
+    summary of the same code: the timed masked launches (not the warmup, not the
+    dense reference), and nothing when the code hash differs."""
+    code = bench.kernel_code_hash("bf16")
+    ghz, note = bench.read_clock(code)
+    assert ghz is not None and 1.0 < ghz < 2.5, (ghz, note)
+    assert bench.read_clock("0" * 16)[0] is None
+    f = tmp_path / "pmc.txt"
+    f.write_text("# header\nkernel_code_sha256_16: abc\n\n"
+                 "dispatch  kernel  dur_ms GHz\n"
+                 "24        <128, 128, true> skip-list       102.42   1.500     63.8%  32.0  57.8%  0.02%  6.18  67.5%\n"
+                 "51        <128, 128, true> skip-list        86.19   1.800     58.4%  32.0  53.6%  0.02%  6.27  29.8%\n"
+                 "53        <128, 128, true> skip-list        85.27   1.900     58.3%  32.0  53.6%  0.02%  6.27  29.7%\n"
+                 "87        <128, 128, false> dense ref       99.71   1.648     68.0%  32.0  60.9%  0.01%  6.08  91.5%\n")
+    monkeypatch.setattr(bench, "PMC_FILE", str(f))
+    ghz, _ = bench.read_clock("abc")
+    assert abs(ghz - 1.85) < 1e-12
+    assert bench.read_clock("abd")[0] is None
